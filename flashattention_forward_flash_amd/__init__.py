@@ -1,0 +1,163 @@
+"""MI355X (gfx950) tiled FlashAttention forward: thin Python binding of ``libfa.so``.
+
+The binding only marshals arguments: every step of the computation runs in the HIP kernels
+of ``csrc/fa_fwd.hip``.  PyTorch supplies device buffers and the current stream.  There is
+no fallback: if the library is missing, importing the functions below raises.
+
+Names follow include/fa.h:
+  ``fa_fwd`` / ``fa_fwd_tiled`` / ``fa_status_str``: the C entry points over raw pointers.
+  ``forward(q, k, v, ...)``: the same call over torch tensors (strides taken from them).
+"""
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfa.so")
+
+FA_OK, FA_EINVAL, FA_ESHAPE, FA_EUNSUPPORTED, FA_EDEVICE = range(5)
+FA_F32, FA_BF16 = 0, 1
+
+
+class FaError(RuntimeError):
+    """A non-OK fa_status; ``.status`` holds the code."""
+
+    def __init__(self, status, msg):
+        super().__init__(f"{msg} (fa_status {status})")
+        self.status = status
+
+
+class fa_strides(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_int64 * 3), ("k", ctypes.c_int64 * 3), ("v", ctypes.c_int64 * 3),
+                ("o", ctypes.c_int64 * 3), ("lse", ctypes.c_int64 * 2), ("mask", ctypes.c_int64 * 4)]
+
+
+class fa_tiling(ctypes.Structure):
+    _fields_ = [("rows_per_block", ctypes.c_int32), ("heads_per_block", ctypes.c_int32)]
+
+
+_lib = None
+_FWD_ARGS = [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int64] * 6 + [
+    ctypes.c_float, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+    ctypes.POINTER(fa_strides), ctypes.c_int, ctypes.c_void_p]
+EXPORTED = ("fa_fwd", "fa_fwd_tiled", "fa_status_str")
+
+
+def load_library(path=None):
+    """Loads libfa.so (built by ``build.build()``); raises ImportError if it is missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing: build it with `python -m flashattention_forward_flash_amd.build` "
+                          "(there is no fallback path)")
+    lib = ctypes.CDLL(p)
+    lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_fwd.argtypes = _FWD_ARGS
+    lib.fa_fwd_tiled.restype = ctypes.c_int
+    lib.fa_fwd_tiled.argtypes = _FWD_ARGS + [ctypes.POINTER(fa_tiling)]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_status_str.argtypes = [ctypes.c_int]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def fa_status_str(status):
+    return load_library().fa_status_str(int(status)).decode()
+
+
+def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, causal, window, sinks, mask,
+           strides, dtype, stream):
+    """The C entry point over raw device pointers (ints or None); returns the fa_status."""
+    return load_library().fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, int(causal),
+                                  window, sinks, mask, strides, dtype, stream)
+
+
+def fa_fwd_tiled(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, causal, window, sinks, mask,
+                 strides, dtype, stream, tiling):
+    return load_library().fa_fwd_tiled(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset,
+                                        int(causal), window, sinks, mask, strides, dtype, stream, tiling)
+
+
+def _check(status):
+    if status != FA_OK:
+        raise FaError(status, fa_status_str(status))
+
+
+def forward(q, k, v, *, scale=None, q_offset=0, causal=True, window=0, sinks=None, mask=None,
+            out=None, lse=None, return_lse=True, tiling=None, stream=None):
+    """O = softmax(scale * Q K^T + mask) V over torch tensors on the GPU.
+
+    q: [B, Hq, Tq, d]; k, v: [B, Hkv, Tk, d]; float32 or bfloat16, any strides with the d axis
+    contiguous (e.g. a [B, T, H, d] tensor viewed with ``.transpose(1, 2)``).  ``mask``: float32
+    tensor broadcastable to [B, Hq, Tq, Tk] (broadcast axes get stride 0).  ``sinks``: float32
+    [Hq].  ``scale`` defaults to 1/sqrt(d) rounded to fp32.  Returns (o, lse) with lse float32
+    [B, Hq, Tq] (None when ``return_lse`` is False and no ``lse`` buffer is given).
+    ``tiling``: (rows_per_block, heads_per_block) or None for automatic; results do not depend
+    on it.
+    """
+    import torch
+    if q.dtype == torch.float32:
+        dtype = FA_F32
+    elif q.dtype == torch.bfloat16:
+        dtype = FA_BF16
+    else:
+        raise FaError(FA_EUNSUPPORTED, f"dtype {q.dtype} (float32 or bfloat16 only)")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise FaError(FA_EINVAL, "q, k and v must share a dtype")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise FaError(FA_EINVAL, "q, k, v must be 4-d [B, H, T, d]")
+    B, Hq, Tq, d = q.shape
+    Bk, Hkv, Tk, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
+        raise FaError(FA_EINVAL, f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.numel() and t.stride(3) != 1:
+            raise FaError(FA_EINVAL, f"{name}: the d axis must be contiguous")
+        if t.numel() and not t.is_cuda:
+            raise FaError(FA_EINVAL, f"{name} must be a GPU tensor")
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    if out is None:
+        out = torch.empty((B, Hq, Tq, d), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    st = fa_strides()
+    st.q[:] = [q.stride(0), q.stride(1), q.stride(2)]
+    st.k[:] = [k.stride(0), k.stride(1), k.stride(2)]
+    st.v[:] = [v.stride(0), v.stride(1), v.stride(2)]
+    st.o[:] = [out.stride(0), out.stride(1), out.stride(2)]
+    if out.numel() and out.stride(3) != 1:
+        raise FaError(FA_EINVAL, "out: the d axis must be contiguous")
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Tq) or (lse.numel() and lse.stride(2) != 1):
+            raise FaError(FA_EINVAL, "lse must be float32 [B, Hq, Tq] with a contiguous last axis")
+        st.lse[:] = [lse.stride(0), lse.stride(1)]
+    mask_ptr = None
+    if mask is not None:
+        if mask.dtype != torch.float32:
+            raise FaError(FA_EINVAL, "mask must be float32")
+        mview = mask.expand(B, Hq, Tq, Tk)
+        st.mask[:] = [mview.stride(i) if mview.shape[i] > 1 else 0 for i in range(4)]
+        mask_ptr = mview.data_ptr() if mview.numel() else None
+    else:
+        st.mask[:] = [0, 0, 0, 0]
+    if sinks is not None:
+        if sinks.dtype != torch.float32 or tuple(sinks.shape) != (Hq,) or not sinks.is_contiguous():
+            raise FaError(FA_EINVAL, "sinks must be a contiguous float32 [Hq] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream if q.is_cuda else None
+
+    def ptr(t):
+        return t.data_ptr() if (t is not None and t.numel()) else None
+
+    til = None
+    if tiling is not None:
+        til = fa_tiling(int(tiling[0]), int(tiling[1]))
+    status = fa_fwd_tiled(ptr(q), ptr(k), ptr(v), ptr(out), ptr(lse), B, Hq, Hkv, Tq, Tk, d, float(scale),
+                          int(q_offset), bool(causal), int(window), ptr(sinks), mask_ptr, ctypes.byref(st),
+                          dtype, stream, ctypes.byref(til) if til is not None else None)
+    _check(status)
+    return out, lse

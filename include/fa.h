@@ -1,0 +1,120 @@
+/*
+ * fa.h -- C ABI of libfa.so, the tiled FlashAttention forward pass for AMD MI355X (gfx950).
+ *
+ * The operation ("FlashAttention forward in C", tinyllm L9.3, section 2.1 "What is
+ * computed", with the additive mask of "Fused attention and softmax: fast and exact",
+ * OneModel, "What is computed"): for every sequence b, query head h and query row i,
+ *
+ *   p_i  = q_offset + i                                   (absolute position of row i)
+ *   V_i  = { j < Tk : (causal == 0 or j <= p_i) and (window <= 0 or j > p_i - window) }
+ *   s_ij = scale * q_i . k_j + mask[b, h, i, j]           (mask term 0 without a mask)
+ *   o_i  = sum_{j in V_i} e^{s_ij} v_j / (sum_{j in V_i} e^{s_ij} + e^{z_h})
+ *   lse_i = log(sum_{j in V_i} e^{s_ij} + e^{z_h})        (natural log)
+ *
+ * where head h reads KV head floor(h / (Hq / Hkv)) (grouped-query attention) and the
+ * e^{z_h} sink term is present only when `sinks` is given.  A mask entry of -inf removes
+ * the key.  A row with no visible key and no sink gets o = 0 and lse = -inf.
+ *
+ * It is computed one absolute key tile [64t, 64t + 64) at a time with the online softmax
+ * of "FlashAttention forward in C" section 2.2 (and "IV.5: Flash attention", "Softmax
+ * without seeing the whole row"); the score matrix is never stored.  Key tiles sit at
+ * absolute positions and each row skips tiles it cannot see (section 2.4), so the bits of
+ * row i depend only on q_i, K, V, p_i, the flags, d and the dtype: not on how the queries
+ * are chunked (q_offset), on the query tile, the batch, the strides or the launch order.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_EINVAL = 1,       /* bad argument: negative size or q_offset, NULL tensor, bad stride, non-finite scale */
+  FA_ESHAPE = 2,       /* head shapes: Hkv == 0 with Hq > 0, Hkv > Hq, or Hq % Hkv != 0 */
+  FA_EUNSUPPORTED = 3, /* d not 64 or 128, unknown dtype, misaligned tensor, size beyond int32 */
+  FA_EDEVICE = 4       /* the HIP launch failed (no device, invalid stream, ...) */
+} fa_status;
+
+typedef enum {
+  FA_F32 = 0,  /* q, k, v, o are fp32; all arithmetic fp32 */
+  FA_BF16 = 1  /* q, k, v, o are bf16; scores and accumulators fp32, weights rounded to bf16 */
+} fa_dtype;
+
+/*
+ * Element strides.  The d axis of q, k, v and o is contiguous (stride 1); the t axis of
+ * lse is contiguous.  Strides must be >= 0.  A stride of 0 in mask broadcasts that axis.
+ */
+typedef struct {
+  int64_t q[3], k[3], v[3], o[3]; /* along (b, h, t) */
+  int64_t lse[2];                 /* along (b, h) */
+  int64_t mask[4];                /* along (b, h, i, j); i is the row of this call */
+} fa_strides;
+
+/*
+ * fa_fwd -- enqueue the forward pass on `stream` and return; results are valid once the
+ * stream has synchronised.
+ *
+ * Pointers are device memory owned by the caller:
+ *   q     [B, Hq,  Tq, d]  dtype       k, v [B, Hkv, Tk, d]  dtype
+ *   o     [B, Hq,  Tq, d]  dtype (written)
+ *   lse   [B, Hq,  Tq]     fp32 (written) or NULL
+ *   sinks [Hq]             fp32 raw logits (not scaled) or NULL
+ *   mask  fp32 additive mask indexed [b, h, i, j] through strides->mask, or NULL
+ * strides == NULL means contiguous [B, H, T, d] tensors, lse [B, Hq, Tq] and a mask of
+ * [Tq, Tk] broadcast over b and h.  scale is taken as given (callers usually pass
+ * 1/sqrt(d) rounded to fp32).  window <= 0 means no window.  stream is a hipStream_t
+ * (NULL: the default stream).
+ *
+ * Alignment: q, k, v and their (b, h, t) strides must be 16-byte aligned; o and its
+ * strides 16-byte aligned for fp32, 8-byte for bf16.
+ *
+ * The library allocates nothing and keeps no state: scratch is on-chip (LDS and
+ * registers) and its size does not depend on Tk.  Calls on different streams may overlap.
+ *
+ * Errors are returned synchronously, before any launch, and leave o and lse untouched:
+ * FA_EINVAL, FA_ESHAPE and FA_EUNSUPPORTED as listed in fa_status.  B * Hq * Tq == 0 returns
+ * FA_OK without a launch.  Tk == 0 is valid (k and v may then be NULL): every row gets
+ * o = 0 and lse = -inf, or lse = the sink logit.  FA_EDEVICE reports a failed launch.
+ */
+fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                 int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                 float scale, int64_t q_offset, int causal, int64_t window,
+                 const float *sinks, const float *mask, const fa_strides *strides,
+                 fa_dtype dtype, void *stream);
+
+/*
+ * Launch geometry.  A workgroup covers `rows_per_block` consecutive query rows of
+ * `heads_per_block` query heads that share one KV head, so each K/V tile staged on chip
+ * serves all of them.  rows_per_block * heads_per_block must be 32, 64 or 128 (one wave per
+ * 32 rows of one head); heads_per_block must divide Hq / Hkv.  0 in both fields picks
+ * automatically (what fa_fwd does).
+ */
+typedef struct {
+  int32_t rows_per_block;
+  int32_t heads_per_block;
+} fa_tiling;
+
+/*
+ * fa_fwd_tiled -- fa_fwd with an explicit launch geometry (tiling may be NULL).  The
+ * results are bit-identical to fa_fwd's for every valid geometry: the geometry only
+ * decides which rows share a workgroup ("FlashAttention forward in C", section 2.4:
+ * results do not depend on the query tile size).  An invalid geometry returns FA_EINVAL.
+ */
+fa_status fa_fwd_tiled(const void *q, const void *k, const void *v, void *o, float *lse,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                       float scale, int64_t q_offset, int causal, int64_t window,
+                       const float *sinks, const float *mask, const fa_strides *strides,
+                       fa_dtype dtype, void *stream, const fa_tiling *tiling);
+
+/* Static English name of a status code (never NULL). */
+const char *fa_status_str(fa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

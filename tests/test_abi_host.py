@@ -1,0 +1,100 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every symbol
+include/fa.h declares, and rejects bad arguments before any launch.
+
+Every call here is one that must fail validation (or has no rows, so nothing is launched):
+no call may reach a kernel launch with these placeholder pointers.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import flashattention_forward_flash_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+P = 0x10000  # an aligned placeholder address; never dereferenced by these calls
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert names == sorted(fa.EXPORTED), names
+    lib = fa.load_library()
+    for n in names:
+        assert hasattr(lib, n), n
+    nm = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(re.findall(r" T (\w+)$", nm.stdout, re.M))
+    assert set(names) <= exported
+
+
+def test_status_strings():
+    for s in range(5):
+        assert fa.fa_status_str(s)
+    assert fa.fa_status_str(99) == "unknown status"
+
+
+def _call(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Hq=4, Hkv=2, Tq=8, Tk=8, d=64, scale=0.125, q_offset=0,
+             causal=1, window=0, sinks=None, mask=None, strides=None, dtype=fa.FA_F32, stream=None)
+    a.update(kw)
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Tq"], a["Tk"],
+                     a["d"], a["scale"], a["q_offset"], a["causal"], a["window"], a["sinks"], a["mask"],
+                     a["strides"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(Hq=6, Hkv=4), fa.FA_ESHAPE),
+    (dict(Hq=2, Hkv=4), fa.FA_ESHAPE),
+    (dict(Hq=4, Hkv=0), fa.FA_ESHAPE),
+    (dict(B=-1), fa.FA_EINVAL),
+    (dict(Tq=-1), fa.FA_EINVAL),
+    (dict(Tk=-5), fa.FA_EINVAL),
+    (dict(q_offset=-1), fa.FA_EINVAL),
+    (dict(d=0), fa.FA_EINVAL),
+    (dict(scale=float("inf")), fa.FA_EINVAL),
+    (dict(scale=float("nan")), fa.FA_EINVAL),
+    (dict(q=None), fa.FA_EINVAL),
+    (dict(o=None), fa.FA_EINVAL),
+    (dict(k=None), fa.FA_EINVAL),
+    (dict(d=96), fa.FA_EUNSUPPORTED),
+    (dict(d=32), fa.FA_EUNSUPPORTED),
+    (dict(dtype=7), fa.FA_EUNSUPPORTED),
+    (dict(q=P + 8), fa.FA_EUNSUPPORTED),          # q not 16-byte aligned
+    (dict(k=P + 4), fa.FA_EUNSUPPORTED),
+    (dict(o=P + 8, dtype=fa.FA_F32), fa.FA_EUNSUPPORTED),
+    (dict(Tq=2**31), fa.FA_EUNSUPPORTED),
+])
+def test_validation_errors(kw, want):
+    assert _call(**kw) == want
+
+
+def test_bad_strides_and_tiling():
+    st = fa.fa_strides()
+    st.q[:] = [8 * 64 * 4, 8 * 64, 64]
+    st.k[:] = st.v[:] = [8 * 64 * 2, 8 * 64, 64]
+    st.o[:] = st.q[:]
+    st.lse[:] = [4 * 8, 8]
+    st.mask[:] = [0, 0, -1, 1]
+    assert _call(strides=ctypes.byref(st)) == fa.FA_EINVAL   # negative mask stride
+    st.mask[:] = [0, 0, 8, 1]
+    st.q[2] = 66                                             # q rows not 16-byte aligned
+    assert _call(strides=ctypes.byref(st)) == fa.FA_EUNSUPPORTED
+    lib = fa.load_library()
+    for til in ((48, 1), (32, 3), (64, 4), (0, 2), (-32, 1)):
+        t = fa.fa_tiling(*til)
+        assert lib.fa_fwd_tiled(P, P, P, P, None, 1, 4, 2, 8, 8, 64, 0.125, 0, 1, 0, None, None, None,
+                                fa.FA_F32, None, ctypes.byref(t)) == fa.FA_EINVAL, til
+
+
+def test_empty_work_returns_ok_without_launch():
+    assert _call(Tq=0) == fa.FA_OK
+    assert _call(B=0) == fa.FA_OK
+    assert _call(Hq=0, Hkv=0, q=None, o=None) == fa.FA_OK
+    assert _call(Tq=0, q=None, o=None, k=None, v=None) == fa.FA_OK
