@@ -1,0 +1,256 @@
+"""Benchmark of the MI355X FlashAttention forward pass.
+
+One step = one fa_fwd call on the large bf16 causal batch (B=8, Hq=32, Hkv=8, Tq=Tk=8192,
+d=128, scale 1/sqrt(128), inputs N(0,1) already resident in HBM).  `value` is attention
+TFLOP/s counted over causal-visible pairs (4 d flops per visible (query, key) pair: 2d for
+the scores, 2d for P V; exp, max and sum not counted) over the wall time of the timed steps.
+
+The same JSON line also reports
+  * roofline: the kernel's average duration from HIP events on its stream, against the
+    MI355X dense bf16 MFMA peak;
+  * prefill_ms: 28 back-to-back calls (one per layer, fresh seeded inputs per layer) at
+    16 query / 8 KV heads, d 128: 511 tokens fp32, 2044 tokens fp32 and bf16;
+  * extra workloads: the 32/8-head d 64 sliding-window (512) prefill with sinks, chunked
+    (1000, 1000, 1000, 1096) and whole, and the non-causal run with a broadcast additive mask;
+  * cpu_baseline: the fp64 oracle timed on the host cores over a bounded row sample of the
+    headline workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk/CU x 2.4 GHz, dense
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd TFLOP/s (causal-visible) + % MFMA peak; prefill ms @511/2044"
+
+
+def visible_pairs(Tq, Tk, q_offset=0, causal=True, window=0):
+    """sum over rows of |V_i| from the interval form of the visible set."""
+    p = np.arange(Tq, dtype=np.int64) + q_offset
+    hi = np.minimum(Tk, p + 1) if causal else np.full(Tq, Tk, np.int64)
+    lo = np.maximum(0, p - window + 1) if window > 0 else np.zeros(Tq, np.int64)
+    return int(np.maximum(0, hi - lo).sum())
+
+
+def _dev(a):
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def _inputs(tag, B, Hq, Hkv, Tq, Tk, d, dtype, layout="bhsd"):
+    import synth
+    if layout == "bshd":
+        q = synth.normal(synth.seed_of(tag, "q"), (B, Tq, Hq, d), dtype)
+        k = synth.normal(synth.seed_of(tag, "k"), (B, Tk, Hkv, d), dtype)
+        v = synth.normal(synth.seed_of(tag, "v"), (B, Tk, Hkv, d), dtype)
+        return tuple(_dev(a).transpose(1, 2) for a in (q, k, v))
+    q = synth.normal(synth.seed_of(tag, "q"), (B, Hq, Tq, d), dtype)
+    k = synth.normal(synth.seed_of(tag, "k"), (B, Hkv, Tk, d), dtype)
+    v = synth.normal(synth.seed_of(tag, "v"), (B, Hkv, Tk, d), dtype)
+    return _dev(q), _dev(k), _dev(v)
+
+
+def _timed(fn, steps, warmup):
+    """Returns (wall ms per step, mean event ms per call) for `steps` calls after `warmup`."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in evs:
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    ev = float(np.mean([s.elapsed_time(e) for s, e in evs]))
+    return wall, ev
+
+
+def bench_headline(steps, warmup):
+    import torch
+    import flashattention_forward_flash_amd as fa
+    B, Hq, Hkv, T, d = 8, 32, 8, 8192, 128
+    q, k, v = _inputs("c5", B, Hq, Hkv, T, T, d, "bf16")
+    scale = float(np.float32(1 / math.sqrt(d)))
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+    print(f"[bench] headline B={B} Hq={Hq} Hkv={Hkv} T={T} d={d} bf16 causal", file=sys.stderr, flush=True)
+    wall, ev = _timed(lambda: fa.forward(q, k, v, scale=scale, causal=True, out=out, lse=lse), steps, warmup)
+    flops = 4.0 * d * B * Hq * visible_pairs(T, T)
+    algo_bytes = 2 * (q.numel() + k.numel() + v.numel() + out.numel()) + 4 * lse.numel()
+    return dict(B=B, Hq=Hq, Hkv=Hkv, T=T, d=d, flops=flops, bytes=algo_bytes, wall_ms=wall, event_ms=ev,
+                q=q, k=k, v=v, scale=scale)
+
+
+def bench_mask_run(h, steps, warmup):
+    """Same inputs, non-causal, fp32 additive mask [8192, 8192] broadcast over b and h (stride 0):
+    10 % of entries -inf, 16 fully masked rows."""
+    import torch
+    import synth
+    import flashattention_forward_flash_amd as fa
+    T = h["T"]
+    m = synth.neg_inf_mask(synth.seed_of("c5", "mask"), (T, T), 0.1)
+    for r in (0, 1, 63, 64, 65, 127, 128, 1023, 1024, 2047, 4095, 4096, 6000, 8127, 8128, 8191):
+        m[r] = -np.inf
+    mask = torch.from_numpy(m).cuda()
+    out = torch.empty_like(h["q"])
+    print("[bench] headline inputs, non-causal, broadcast additive mask", file=sys.stderr, flush=True)
+    wall, ev = _timed(lambda: fa.forward(h["q"], h["k"], h["v"], scale=h["scale"], causal=False, mask=mask,
+                                         out=out), steps, warmup)
+    flops = 4.0 * h["d"] * h["B"] * h["Hq"] * T * T
+    return dict(ms=ev, tflops=flops / (ev * 1e-3) / 1e12)
+
+
+def bench_prefill(T, dtype, layers=28, reps=5):
+    """28 calls (one per layer) at 16/8 heads, d 128, in the concatenated-heads layout."""
+    import torch
+    import flashattention_forward_flash_amd as fa
+    Hq, Hkv, d = 16, 8, 128
+    per_layer = [_inputs(f"prefill{T}/{dtype}/{layer}", 1, Hq, Hkv, T, T, d, dtype, layout="bshd")
+                 for layer in range(layers)]
+    outs = [torch.empty((1, T, Hq, d), dtype=per_layer[0][0].dtype, device="cuda").transpose(1, 2)
+            for _ in range(layers)]
+    scale = float(np.float32(1 / math.sqrt(d)))
+
+    def run_all():
+        for (q, k, v), o in zip(per_layer, outs):
+            fa.forward(q, k, v, scale=scale, causal=True, out=o, return_lse=False)
+
+    print(f"[bench] prefill T={T} {dtype} x{layers} layers", file=sys.stderr, flush=True)
+    wall, ev = _timed(run_all, reps, 2)
+    flops = 4.0 * d * Hq * visible_pairs(T, T) * layers
+    peak = PEAK_F32_TFLOPS if dtype == "f32" else PEAK_BF16_TFLOPS
+    return dict(ms=round(ev, 4), per_call_ms=round(ev / layers, 5), tflops=round(flops / (ev * 1e-3) / 1e12, 2),
+                frac_peak=round(flops / (ev * 1e-3) / 1e12 / peak, 4))
+
+
+def bench_window_chunks(steps=10, warmup=3):
+    """32/8 heads, d 64, Tk 4096, window 512, sinks, causal, fp32: one call and 4 chunks."""
+    import torch
+    import synth
+    import flashattention_forward_flash_amd as fa
+    Hq, Hkv, T, d = 32, 8, 4096, 64
+    q, k, v = _inputs("c4", 1, Hq, Hkv, T, T, d, "f32")
+    z = torch.from_numpy(synth.normal_f32(synth.seed_of("c4", "z"), (Hq,))).cuda()
+    scale = float(np.float32(1 / math.sqrt(d)))
+    out = torch.empty_like(q)
+    lse = torch.empty((1, Hq, T), dtype=torch.float32, device="cuda")
+    print("[bench] sliding window with sinks, whole and chunked", file=sys.stderr, flush=True)
+    _, ev_full = _timed(lambda: fa.forward(q, k, v, scale=scale, causal=True, window=512, sinks=z, out=out, lse=lse),
+                        steps, warmup)
+    chunks = [(0, 1000), (1000, 1000), (2000, 1000), (3000, 1096)]
+
+    def run_chunks():
+        for s, n in chunks:
+            fa.forward(q[:, :, s:s + n], k, v, scale=scale, q_offset=s, causal=True, window=512, sinks=z,
+                       out=out[:, :, s:s + n], lse=lse[:, :, s:s + n])
+
+    _, ev_chunks = _timed(run_chunks, steps, warmup)
+    flops = 4.0 * d * Hq * visible_pairs(T, T, 0, True, 512)
+    return dict(ms=round(ev_full, 4), chunked_ms=round(ev_chunks, 4),
+                tflops=round(flops / (ev_full * 1e-3) / 1e12, 2))
+
+
+def cpu_baseline(h, target_s=15.0):
+    """The fp64 oracle on the host cores over a seeded row sample of the headline workload,
+    scaled to the metric's unit (TFLOP/s over the sampled rows' visible pairs)."""
+    import oracle
+    B, Hq, T, d = h["B"], h["Hq"], h["T"], h["d"]
+    q = h["q"].view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    k = h["k"].view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    v = h["v"].view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    cores = len(os.sched_getaffinity(0))
+    oracle.attention(q[:1, :1, :1], k[:1, :1, :1], v[:1, :1, :1], scale=h["scale"], threads=cores)
+    cores = oracle.threads()
+    rng = np.random.default_rng(5)
+    n = 256
+    while True:
+        rows = np.stack([rng.integers(0, B, n), rng.integers(0, Hq, n), rng.integers(0, T, n)], 1)
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, scale=h["scale"], causal=True, rows=rows, threads=cores)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 4 or n >= (1 << 20):
+            break
+        n = int(n * min(16.0, max(2.0, target_s / max(dt, 1e-3))))
+    pairs = int(np.sum(rows[:, 2] + 1))
+    flops = 4.0 * d * pairs
+    return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=cores, kind="oracle",
+                sample=f"{n} seeded (b, h, i) rows of the headline workload ({pairs} visible pairs, fp64), "
+                       f"{dt:.1f} s wall",
+                seconds=round(dt, 2))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--headline-only", action="store_true", help="skip the prefill / window / mask / CPU legs")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the pass shards over (b, head group) or "
+              "query tiles with no exchange; multi-GPU runs are not part of it). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import flashattention_forward_flash_amd as fa
+    fa.load_library()
+    torch.cuda.init()
+
+    h = bench_headline(args.steps, args.warmup)
+    tflops = h["flops"] / (h["wall_ms"] * 1e-3) / 1e12
+    achieved = h["flops"] / (h["event_ms"] * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["wall_ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal bf16 batch: B=8, Hq=32, Hkv=8, Tq=Tk=8192, d=128, scale 1/sqrt(128), "
+                               "N(0,1) inputs, fp32 accumulate, bf16 O + fp32 LSE",
+                   "global_batch": 8, "seq_len": 8192, "parallelism": "none (1 GPU)"},
+        "frac_mfma_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "kernel_ms": round(h["event_ms"], 4),
+        "algorithmic_bytes": h["bytes"],
+    }
+    if not args.headline_only:
+        m = bench_mask_run(h, max(3, args.steps // 4), 2)
+        result["mask_run"] = {"ms": round(m["ms"], 4), "tflops": round(m["tflops"], 2),
+                              "frac_mfma_peak": round(m["tflops"] / PEAK_BF16_TFLOPS, 4)}
+        torch.cuda.empty_cache()
+        result["prefill_ms"] = {
+            "511_f32_28L": bench_prefill(511, "f32"),
+            "2044_f32_28L": bench_prefill(2044, "f32"),
+            "2044_bf16_28L": bench_prefill(2044, "bf16"),
+        }
+        result["window_sinks_4096"] = bench_window_chunks()
+    if not args.no_cpu and not args.headline_only:
+        result["cpu_baseline"] = cpu_baseline(h)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

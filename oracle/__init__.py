@@ -39,6 +39,9 @@ def _load(path=None):
             ctypes.c_void_p, ctypes.c_void_p, i64p, ctypes.c_void_p, ctypes.c_int64,
             ctypes.c_void_p, ctypes.c_void_p,
         ]
+        lib.orc_set_threads.argtypes = [ctypes.c_int]
+        lib.orc_set_threads.restype = None
+        lib.orc_max_threads.restype = ctypes.c_int
         lib.orc_visible_pairs.restype = ctypes.c_int64
         lib.orc_visible_pairs.argtypes = [ctypes.c_int64] * 3 + [ctypes.c_int, ctypes.c_int64]
         _LIBS[path] = lib
@@ -84,8 +87,6 @@ def attention(q, k, v, *, scale, q_offset=0, causal=True, window=0, sinks=None, 
     Bk, Hkv, Tk, dk = k.shape
     if v.shape != k.shape or Bk != B or dk != d:
         raise ValueError("shape mismatch")
-    if threads is not None:
-        os.environ["OMP_NUM_THREADS"] = str(threads)
     sk_ = _strides(k, 4)
     if Tk == 0:
         k = v = np.zeros((1, 1, 1, d), q.dtype)
@@ -107,6 +108,8 @@ def attention(q, k, v, *, scale, q_offset=0, causal=True, window=0, sinks=None, 
     o = np.empty(o_shape, np.float64)
     lse = np.empty(l_shape, np.float64)
     lib = _load(lib_path)
+    if threads is not None:
+        lib.orc_set_threads(int(threads))
     rc = lib.orc_attention(
         q.ctypes.data, _strides(q, 4), k.ctypes.data, _strides(k, 4) if Tk else sk_, v.ctypes.data,
         _strides(v, 4) if Tk else sk_, dtype, B, Hq, Hkv, Tq, Tk, d, float(np.float64(scale)),
@@ -123,3 +126,8 @@ def attention(q, k, v, *, scale, q_offset=0, causal=True, window=0, sinks=None, 
 def visible_pairs(Tq, Tk, q_offset=0, causal=True, window=0):
     """sum_i |V_i| for one (b, h): the pairs the FLOP count is taken over."""
     return int(_load().orc_visible_pairs(Tq, Tk, q_offset, int(bool(causal)), window))
+
+
+def threads():
+    """OpenMP threads the oracle's row loop uses."""
+    return int(_load().orc_max_threads())

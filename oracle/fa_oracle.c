@@ -30,6 +30,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #ifndef ORACLE_MUTANT
 #define ORACLE_MUTANT 0
@@ -192,6 +195,22 @@ int orc_attention(const void *q, const int64_t *sq, const void *k, const int64_t
     free(s);
   }
   return bad ? -1 : 0;
+}
+
+/* Thread control for the OpenMP row loop (host-side timing of the oracle). */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+int orc_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }
 
 /* Number of visible (query, key) pairs of one (b, h): sum_i |V_i| (mask not counted). */

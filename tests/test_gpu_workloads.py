@@ -1,0 +1,145 @@
+"""GPU parity at the full workload sizes, in the launch configuration the bench times
+(automatic geometry), against the fp64 oracle: whole calls where the oracle finishes in
+seconds, seeded row samples (tile-boundary rows included) where it does not.
+
+Workloads (inputs N(0, 1) from the seeded generator; shapes of "IV.5: Flash attention",
+"Running it": 28 layers, 16 query / 8 KV heads, d 128, 511 and 2,044 tokens; the sliding
+window with sinks and chunked prefill of "FlashAttention forward in C"; the broadcast
+additive mask of "Fused attention and softmax: fast and exact").
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import flashattention_forward_flash_amd as fa
+import oracle
+import synth
+from gpu_common import bits, compare, dev, host, sample_rows, say, scale_for
+
+pytestmark = pytest.mark.gpu
+
+
+def _bshd_inputs(tag, T, dtype, Hq=16, Hkv=8, d=128):
+    q = synth.normal(synth.seed_of(tag, "q"), (1, T, Hq, d), dtype)
+    k = synth.normal(synth.seed_of(tag, "k"), (1, T, Hkv, d), dtype)
+    v = synth.normal(synth.seed_of(tag, "v"), (1, T, Hkv, d), dtype)
+    return q, k, v
+
+
+def _prefill(T, dtype, full_layers, sample_per_layer=48):
+    """28 layers of the concatenated-heads prefill; full parity on `full_layers`, a row sample
+    on the others."""
+    d, Hq = 128, 16
+    sc = scale_for(d)
+    for layer in range(28):
+        q, k, v = _bshd_inputs(f"prefill{T}/{dtype}/{layer}", T, dtype)
+        tq, tk, tv = (dev(a).transpose(1, 2) for a in (q, k, v))
+        out = torch.empty((1, T, Hq, d), dtype=tq.dtype, device="cuda").transpose(1, 2)
+        say("prefill", T, dtype, "layer", layer)
+        o, lse = fa.forward(tq, tk, tv, scale=sc, causal=True, out=out)
+        torch.cuda.synchronize()
+        qo, ko, vo = (a.transpose(0, 2, 1, 3) for a in (q, k, v))  # strided views for the oracle
+        if layer in full_layers:
+            o_ref, l_ref = oracle.attention(qo, ko, vo, scale=sc, causal=True)
+            compare(host(o), host(lse), o_ref, l_ref, dtype, f"prefill{T} layer {layer}")
+        else:
+            rows = sample_rows(1, Hq, T, sample_per_layer, seed=layer)
+            o_ref, l_ref = oracle.attention(qo, ko, vo, scale=sc, causal=True, rows=rows)
+            og, lg = host(o), host(lse)
+            compare(og[rows[:, 0], rows[:, 1], rows[:, 2]], lg[rows[:, 0], rows[:, 1], rows[:, 2]],
+                    o_ref, l_ref, dtype, f"prefill{T} layer {layer} (rows)")
+
+
+def test_prefill_511_fp32_28_layers():
+    _prefill(511, "f32", full_layers=(0, 13, 27))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_2044_28_layers(dtype):
+    _prefill(2044, dtype, full_layers=(0,))
+
+
+def test_window_sinks_chunked_bitwise_and_parity():
+    """32/8 heads, d 64, Tk 4096, window 512, one sink per head, causal, fp32, LSE on:
+    chunks of 1000, 1000, 1000, 1096 at q_offset 0, 1000, 2000, 3000 equal one Tq = 4096
+    call bit for bit, and both match the oracle."""
+    Hq, Hkv, T, d = 32, 8, 4096, 64
+    q = synth.normal(synth.seed_of("c4", "q"), (1, Hq, T, d), "f32")
+    k = synth.normal(synth.seed_of("c4", "k"), (1, Hkv, T, d), "f32")
+    v = synth.normal(synth.seed_of("c4", "v"), (1, Hkv, T, d), "f32")
+    z = synth.normal_f32(synth.seed_of("c4", "z"), (Hq,))
+    sc = scale_for(d)
+    tq, tk, tv, tz = dev(q), dev(k), dev(v), dev(z)
+    say("window-sinks whole")
+    o_full, l_full = fa.forward(tq, tk, tv, scale=sc, causal=True, window=512, sinks=tz)
+    start = 0
+    for n in (1000, 1000, 1000, 1096):
+        say("window-sinks chunk", start, n)
+        o, lse = fa.forward(tq[:, :, start:start + n], tk, tv, scale=sc, q_offset=start, causal=True,
+                            window=512, sinks=tz)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(o), bits(o_full[:, :, start:start + n])), f"O chunk at {start}"
+        assert np.array_equal(bits(lse), bits(l_full[:, :, start:start + n])), f"LSE chunk at {start}"
+        start += n
+    o_ref, l_ref = oracle.attention(q, k, v, scale=sc, causal=True, window=512, sinks=z)
+    compare(host(o_full), host(l_full), o_ref, l_ref, "f32", "window-sinks 4096")
+
+
+@pytest.fixture(scope="module")
+def big_batch():
+    B, Hq, Hkv, T, d = 8, 32, 8, 8192, 128
+    say("big batch inputs", (B, Hq, Hkv, T, d))
+    q = synth.normal(synth.seed_of("c5", "q"), (B, Hq, T, d), "bf16")
+    k = synth.normal(synth.seed_of("c5", "k"), (B, Hkv, T, d), "bf16")
+    v = synth.normal(synth.seed_of("c5", "v"), (B, Hkv, T, d), "bf16")
+    return dict(q=q, k=k, v=v, tq=dev(q), tk=dev(k), tv=dev(v), B=B, Hq=Hq, T=T, d=d)
+
+
+def test_big_batch_causal_bf16_sampled(big_batch):
+    """B=8, 32/8 heads, T=8192, d=128, bf16, causal: 384 sampled rows against the oracle,
+    plus properties over every row (finite, |o| <= max |v|, lse >= the row's own score)."""
+    g = big_batch
+    sc = scale_for(g["d"])
+    say("big batch causal bf16")
+    o, lse = fa.forward(g["tq"], g["tk"], g["tv"], scale=sc, causal=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    vmax = float(g["tv"].abs().max())
+    assert float(o.abs().max()) <= vmax * (1 + 2 ** -7)
+    rows = sample_rows(g["B"], g["Hq"], g["T"], 384, seed=5, extra_i=(255, 256, 4095, 4096, 8190))
+    o_ref, l_ref = oracle.attention(g["q"], g["k"], g["v"], scale=sc, causal=True, rows=rows)
+    og, lg = host(o), host(lse)
+    compare(og[rows[:, 0], rows[:, 1], rows[:, 2]], lg[rows[:, 0], rows[:, 1], rows[:, 2]], o_ref, l_ref,
+            "bf16", "big batch causal (rows)")
+    # row 0 sees only key 0: o = v_0 exactly (its weight is exp2(0) = 1)
+    kv0 = g["tv"][:, :, 0].repeat_interleave(g["Hq"] // g["tv"].shape[1], dim=1)
+    assert torch.equal(o[:, :, 0], kv0)
+
+
+def test_big_batch_broadcast_mask_sampled(big_batch):
+    """Same inputs, non-causal, fp32 mask [8192, 8192] broadcast over b and h (stride 0), 10 %
+    -inf and 16 fully masked rows: sampled rows (every fully masked row included) match the
+    oracle; fully masked rows give O = 0 and LSE = -inf exactly."""
+    g = big_batch
+    T = g["T"]
+    sc = scale_for(g["d"])
+    dead = (0, 1, 63, 64, 65, 127, 128, 1023, 1024, 2047, 4095, 4096, 6000, 8127, 8128, 8191)
+    m = synth.neg_inf_mask(synth.seed_of("c5", "mask"), (T, T), 0.1)
+    for r in dead:
+        m[r] = -np.inf
+    say("big batch broadcast mask")
+    o, lse = fa.forward(g["tq"], g["tk"], g["tv"], scale=sc, causal=False, mask=dev(m))
+    torch.cuda.synchronize()
+    dead_t = torch.tensor(dead, device="cuda")
+    assert torch.all(o[:, :, dead_t] == 0) and torch.all(lse[:, :, dead_t] == -float("inf"))
+    live = torch.ones(T, dtype=torch.bool, device="cuda")
+    live[dead_t] = False
+    assert torch.isfinite(lse[:, :, live]).all() and torch.isfinite(o).all()
+    rows = sample_rows(g["B"], g["Hq"], T, 256, seed=9, extra_i=dead)
+    o_ref, l_ref = oracle.attention(g["q"], g["k"], g["v"], scale=sc, causal=False,
+                                    mask=m[None, None], rows=rows)
+    og, lg = host(o), host(lse)
+    compare(og[rows[:, 0], rows[:, 1], rows[:, 2]], lg[rows[:, 0], rows[:, 1], rows[:, 2]], o_ref, l_ref,
+            "bf16", "big batch mask (rows)")
