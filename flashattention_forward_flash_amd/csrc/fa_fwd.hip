@@ -93,134 +93,77 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 }
 
 // ---------------------------------------------------------------------------------------
-// LDS layouts.
-//  bf16 K: [64 keys][D], 16-byte chunks XOR-swizzled by key % (D/8).
-//  bf16 V^T: [D][64 keys], keys permuted within each group of 16 so that the 8 keys one
-//    lane feeds to one MFMA are contiguous; 16-byte chunks XOR-swizzled by d % 8.
-//  fp32 K: [64 keys][D], 16-byte chunks XOR-swizzled by key % 16.
-//  fp32 V: [64 keys][D], d XOR-swizzled by 32 * bit 2 of the key (the two lane halves read
-//    keys 4 apart and the same d, so they land in different banks).
+// K/V tiles go from HBM straight into LDS (global_load_lds, 16 bytes per lane: lane l of
+// the wave writes bytes [16 l, 16 l + 16) of a 1 KiB LDS block), so no registers hold them
+// and nothing is transposed on the way.  Both tiles are row-major [64 keys][D] in LDS with
+// the 16-byte chunks of each row XOR-swizzled so that the MFMA operand reads are spread
+// over the LDS banks:
+//   K (read 16 bytes per lane, 32 rows at a time): chunk ^ (key % min(chunks per row, 16)).
+//   bf16 V (read with ds_read_b64_tr_b16, 8 keys x 64 bytes at a time): chunk ^ 4 (key % 4)
+//     for d = 128, chunk ^ 4 ((key / 2) % 2) for d = 64.
+//   fp32 V (read 4 bytes per lane; the two lane halves read keys 4 apart): chunk ^ 8 * bit 2
+//     of the key.
+// Rows past Tk are loaded from row Tk - 1 (real, finite data): their scores are replaced by
+// -inf and their weights are 0, so they add nothing.
 // ---------------------------------------------------------------------------------------
 
-// Position of key offset k (0..15) inside its group of 16 in the bf16 V^T layout: the MFMA
-// B-operand slot (8 * half + j) of the S^T register that holds key k (see PV below).
-__device__ __forceinline__ int vt_pos16(int k) { return 8 * ((k >> 2) & 1) + 4 * (k >> 3) + (k & 3); }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 
-template <bool BF16, int D, int NW>
-struct TileIO {
+__device__ __forceinline__ void g2l16(const unsigned char *g, unsigned char *lds_block) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                   (__attribute__((address_space(3))) void *)lds_block, 16, 0, 0);
+}
+
+// ds_read_b64_tr_b16 at LDS byte address `addr`.  Within each group of 16 lanes, lane r
+// supplies 4 consecutive 16-bit elements; lane i receives element i % 4 of the chunks of lanes
+// i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4.  Issued as inline assembly: the compiler's own
+// form is treated as possibly reading the LDS buffer that the next tile is being copied into,
+// and would wait for that copy.  The caller waits for the result with lds_wait().
+template <int OFFSET>
+__device__ __forceinline__ s16x4 lds_read_tr16(uint32_t addr) {
+  static_assert(OFFSET >= 0 && OFFSET < 65536, "ds offset field is 16 bits");
+  s16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFFSET));
+  return r;
+}
+// Waits for every outstanding LDS read of this wave; the operands tie the wait to the values
+// it guards, so their uses cannot move above it.
+__device__ __forceinline__ void lds_wait(s16x4 &a, s16x4 &b, s16x4 &c, s16x4 &d, s16x4 &e, s16x4 &f,
+                                         s16x4 &g, s16x4 &h) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h));
+}
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)p;
+}
+
+template <bool BF16, int D>
+struct Layout {
   static constexpr int ES = BF16 ? 2 : 4;
-  static constexpr int NT = NW * 64;
-  static constexpr int CH = D * ES / 16;              // 16-byte chunks per row
-  static constexpr int K_TASKS = kBc * CH;            // one task = one 16-byte chunk of K
-  static constexpr int K_PER = (K_TASKS + NT - 1) / NT;
-  // V tasks: bf16 = 4 keys x 8 d (transposed on the way to LDS); fp32 = one 16-byte chunk.
-  static constexpr int V_TASKS = BF16 ? (kBc / 4) * (D / 8) : K_TASKS;
-  static constexpr int V_PER = (V_TASKS + NT - 1) / NT;
-  static constexpr int V_REGS = BF16 ? 4 : 1;         // 16-byte registers per V task
+  static constexpr int CH = D * ES / 16;      // 16-byte chunks per row
+  static constexpr int RB = 64 / CH;          // rows per 1 KiB block
+  static constexpr int NBLK = kBc / RB;       // 1 KiB blocks per tile (per tensor)
   static constexpr int TILE_BYTES = kBc * D * ES;
-  // Register-prefetch the next tile (two LDS buffers) when it fits in 64 VGPRs; otherwise
-  // copy each tile straight through one LDS buffer.
-  static constexpr bool PIPE = (K_PER + V_PER * V_REGS) <= 16;
-  static constexpr int LDS_BYTES = (PIPE ? 4 : 2) * TILE_BYTES;
-
-  u32x4 kr[PIPE ? K_PER : 1];
-  u32x4 vr[PIPE ? V_PER * V_REGS : 1];
-
-  __device__ static __forceinline__ u32x4 ld_row(const Params &p, const unsigned char *base, int64_t st,
-                                                 int key, int ch) {
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (key < p.Tk) val = *reinterpret_cast<const u32x4 *>(base + ((int64_t)key * st) * ES + ch * 16);
-    return val;  // rows past Tk are zero: 0 * weight 0 stays 0
-  }
-  __device__ static __forceinline__ u32x4 ld_k(const Params &p, const unsigned char *kbase, int key0, int c) {
-    if (c >= K_TASKS) return u32x4{0u, 0u, 0u, 0u};
-    return ld_row(p, kbase, p.sk_t, key0 + c / CH, c % CH);
-  }
-  __device__ static __forceinline__ void st_k(unsigned char *kl, int c, u32x4 val) {
-    if (c >= K_TASKS) return;
-    const int key = c / CH, ch = c % CH;
-    const int sw = BF16 ? (key % CH) : (key & 15);
-    *reinterpret_cast<u32x4 *>(kl + key * (D * ES) + ((ch ^ sw) * 16)) = val;
-  }
-  __device__ static __forceinline__ void ld_v(const Params &p, const unsigned char *vbase, int key0, int task,
-                                              u32x4 *out) {
-    if constexpr (BF16) {
-      const int g4 = task / (D / 8), dch = task % (D / 8);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        out[kk] = task < V_TASKS ? ld_row(p, vbase, p.sv_t, key0 + 4 * g4 + kk, dch) : u32x4{0u, 0u, 0u, 0u};
-    } else {
-      out[0] = task < V_TASKS ? ld_row(p, vbase, p.sv_t, key0 + task / CH, task % CH) : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ static __forceinline__ void st_v(unsigned char *vl, int task, const u32x4 *in) {
-    if (task >= V_TASKS) return;
-    if constexpr (BF16) {
-      const int g4 = task / (D / 8), dch = task % (D / 8);
-      const int key0 = 4 * g4;                   // 4 consecutive keys, 8 consecutive d
-      const int grp = key0 >> 4, pos = vt_pos16(key0 & 15);
-      const int lchunk = 2 * grp + (pos >> 3);    // logical 16-byte chunk of the V^T row
-      const int hoff = ((pos >> 2) & 1) * 8;      // which 8 bytes of that chunk
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int dd = (s + dch) & 7;             // rotate to spread LDS banks
-        const int d = dch * 8 + dd;
-        uint32_t e[4];                            // element dd of each key: word dd/2, half dd%2
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const uint32_t w = in[kk][dd >> 1];
-          e[kk] = (dd & 1) ? (w >> 16) : (w & 0xFFFFu);
-        }
-        const u32x2 pk = {e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
-        *reinterpret_cast<u32x2 *>(vl + d * (kBc * 2) + ((lchunk ^ (d & 7)) * 16) + hoff) = pk;
-      }
-    } else {
-      const int key = task / CH, ch = task % CH;
-      const int d = (ch * 4) ^ (((key >> 2) & 1) << 5);
-      *reinterpret_cast<u32x4 *>(vl + (key * D + d) * 4) = in[0];
-    }
-  }
-
-  // PIPE: global -> registers for tile t ...
-  __device__ __forceinline__ void load(const Params &p, const unsigned char *kbase, const unsigned char *vbase,
-                                       int t, int tid) {
-    if constexpr (PIPE) {
-#pragma unroll
-      for (int r = 0; r < K_PER; ++r) kr[r] = ld_k(p, kbase, t * kBc, tid + r * NT);
-#pragma unroll
-      for (int r = 0; r < V_PER; ++r) ld_v(p, vbase, t * kBc, tid + r * NT, &vr[r * V_REGS]);
-    }
-  }
-  // ... registers -> LDS
-  __device__ __forceinline__ void store(unsigned char *kl, unsigned char *vl, int tid) const {
-    if constexpr (PIPE) {
-#pragma unroll
-      for (int r = 0; r < K_PER; ++r) st_k(kl, tid + r * NT, kr[r]);
-#pragma unroll
-      for (int r = 0; r < V_PER; ++r) st_v(vl, tid + r * NT, &vr[r * V_REGS]);
-    }
-  }
-  // !PIPE: global -> LDS one task at a time
-  __device__ static __forceinline__ void copy(const Params &p, const unsigned char *kbase,
-                                              const unsigned char *vbase, int t, int tid,
-                                              unsigned char *kl, unsigned char *vl) {
-#pragma unroll 4
-    for (int r = 0; r < K_PER; ++r) st_k(kl, tid + r * NT, ld_k(p, kbase, t * kBc, tid + r * NT));
-#pragma unroll 2
-    for (int r = 0; r < V_PER; ++r) {
-      u32x4 tmp[V_REGS];
-      ld_v(p, vbase, t * kBc, tid + r * NT, tmp);
-      st_v(vl, tid + r * NT, tmp);
-    }
+  __device__ static __forceinline__ int ksw(int key) { return key % (CH < 16 ? CH : 16); }
+  __device__ static __forceinline__ int vsw(int key) {
+    if constexpr (!BF16) return ((key >> 2) & 1) << 3;
+    else if constexpr (D == 128) return 4 * (key & 3);
+    else return 4 * ((key >> 1) & 1);
   }
 };
 
-template <bool BF16, int D, int NW, bool MASK>
-__global__ void __launch_bounds__(NW * 64) fa_fwd_kernel(Params p) {
-  using IO = TileIO<BF16, D, NW>;
-  constexpr int ES = IO::ES;
+template <bool BF16, int D, int NW, int MODE>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 1)))
+fa_fwd_kernel(Params p) {
+  using L = Layout<BF16, D>;
+  constexpr int ES = L::ES;
   constexpr int NDB = D / 32;  // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) unsigned char smem[IO::LDS_BYTES];
+  constexpr int BPW = L::NBLK / NW;  // 1 KiB blocks each wave copies per tensor per tile
+  static_assert(L::NBLK % NW == 0, "blocks per tile must split evenly over the waves");
+  // Two LDS buffers as two objects (each [K | V]), so that the compiler can tell the copy into
+  // one from the reads of the other and does not wait for the copy before those reads.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem0[2 * L::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem1[2 * L::TILE_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int half = lane >> 5, lq = lane & 31;
@@ -249,7 +192,7 @@ __global__ void __launch_bounds__(NW * 64) fa_fwd_kernel(Params p) {
     const int64_t lo = vis_lo(p.q_offset + row0_blk, p), hi = vis_hi(p.q_offset + last, p);
     if (hi > lo) { t_begin = (int)(lo / kBc); t_end = (int)((hi + kBc - 1) / kBc); }
   }
-  int w_begin = 0, w_end = 0;    // this wave's visible tiles
+  int w_begin = 0, w_end = 0;        // this wave's visible tiles
   int64_t full_lo = 1, full_hi = 0;  // tiles inside [full_lo, full_hi) are visible to all its rows
   if (row0_wave < p.Tq) {
     const int last = min(row0_wave + kRowsWave, p.Tq) - 1;
@@ -300,25 +243,29 @@ __global__ void __launch_bounds__(NW * 64) fa_fwd_kernel(Params p) {
                                ((int64_t)b * p.sk_b + (int64_t)kvh * p.sk_h) * ES;
   const unsigned char *vbase = static_cast<const unsigned char *>(p.v) +
                                ((int64_t)b * p.sv_b + (int64_t)kvh * p.sv_h) * ES;
-  const float *mrow = MASK ? p.mask + (int64_t)b * p.sm_b + (int64_t)head * p.sm_h + (int64_t)row * p.sm_i
-                           : nullptr;
+  const float *mrow = MODE == 1 && p.mask
+                          ? p.mask + (int64_t)b * p.sm_b + (int64_t)head * p.sm_h + (int64_t)row * p.sm_i
+                          : nullptr;
 
-  IO io;
-  if (IO::PIPE && t_begin < t_end) {
-    io.load(p, kbase, vbase, t_begin, tid);
-    io.store(smem, smem + IO::TILE_BYTES, tid);
-    __syncthreads();
-  }
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = IO::PIPE ? (t - t_begin) & 1 : 0;
-    unsigned char *kl = smem + buf * 2 * IO::TILE_BYTES;
-    unsigned char *vl = kl + IO::TILE_BYTES;
-    if constexpr (IO::PIPE) {
-      if (t + 1 < t_end) io.load(p, kbase, vbase, t + 1, tid);
-    } else {
-      IO::copy(p, kbase, vbase, t, tid, kl, vl);
-      __syncthreads();
+  // This lane's part of the tile copy: row (block * RB + lane / CH), stored chunk lane % CH.
+  const int cp_row = lane / L::CH, cp_chunk = lane % L::CH;
+  auto issue_tile = [&](int t, unsigned char *kl) {
+    unsigned char *vl = kl + L::TILE_BYTES;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int blk = wid * BPW + i;
+      const int r = blk * L::RB + cp_row;
+      int key = t * kBc + r;
+      key = key < p.Tk ? key : p.Tk - 1;
+      g2l16(kbase + (int64_t)key * p.sk_t * ES + ((cp_chunk ^ L::ksw(r)) * 16), kl + blk * 1024);
+      g2l16(vbase + (int64_t)key * p.sv_t * ES + ((cp_chunk ^ L::vsw(r)) * 16), vl + blk * 1024);
     }
+  };
+
+  // One tile of work: wait-free reads of `kl` (tile t), copy of tile t + 1 into `kn`.
+  auto step = [&](int t, const unsigned char *kl, unsigned char *kn) {
+    const unsigned char *vl = kl + L::TILE_BYTES;
+    if (t + 1 < t_end) issue_tile(t + 1, kn);  // that buffer was released by the last barrier
 
     if (t >= w_begin && t < w_end) {
       // ---- S^T = K Q^T for two 32-key blocks; lane holds key 32kb + 8(i/4) + 4 half + i%4 ----
@@ -332,14 +279,14 @@ __global__ void __launch_bounds__(NW * 64) fa_fwd_kernel(Params p) {
         if constexpr (BF16) {
 #pragma unroll
           for (int ds = 0; ds < D / 16; ++ds) {
-            const int ch = (2 * ds + half) ^ (key % IO::CH);
+            const int ch = (2 * ds + half) ^ L::ksw(key);
             const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kl + key * (D * 2) + ch * 16);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ds], acc, 0, 0, 0);
           }
         } else {
 #pragma unroll
           for (int c = 0; c < D / 8; ++c) {
-            const int ch = (half * (D / 8) + c) ^ (key & 15);
+            const int ch = (half * (D / 8) + c) ^ L::ksw(key);
             const f32x4 a4 = *reinterpret_cast<const f32x4 *>(kl + key * (D * 4) + ch * 16);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -349,38 +296,40 @@ __global__ void __launch_bounds__(NW * 64) fa_fwd_kernel(Params p) {
         sacc[kb] = acc;
       }
 
-      // ---- scores in base-2 units; invisible keys -> -inf by select ----
-      float x[2][16];
+      // ---- scores; keys a row cannot see become -inf by select ----
+      // MODE 0 (no mask, scale > 0): the row maximum is taken on the raw dot products (scaling
+      //   by a positive constant commutes with max and with fp32 rounding), and each weight is
+      //   exp2(fma(s, scale log2 e, -m)).
+      // MODE 1 (additive mask, or scale <= 0): x = fma(s, scale log2 e, mask log2 e) first.
       const bool full = (int64_t)t * kBc >= full_lo && (int64_t)t * kBc + kBc <= full_hi;
+      if constexpr (MODE == 1) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = t * kBc + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          if constexpr (MASK) {
-            const float mv = (row_ok && key < p.Tk) ? mrow[(int64_t)key * p.sm_j] : 0.f;
-            x[kb][i] = __builtin_fmaf(sacc[kb][i], p.scale_log2, mv * kLog2e);
-          } else {
-            x[kb][i] = sacc[kb][i] * p.scale_log2;
+          for (int i = 0; i < 16; ++i) {
+            const int key = t * kBc + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+            const float mv = (mrow && row_ok && key < p.Tk) ? mrow[(int64_t)key * p.sm_j] : 0.f;
+            sacc[kb][i] = __builtin_fmaf(sacc[kb][i], p.scale_log2, mv * kLog2e);
           }
-        }
+      }
       if (!full) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int64_t key = (int64_t)t * kBc + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-            x[kb][i] = (key >= r_lo && key < r_hi) ? x[kb][i] : -INFINITY;
+            sacc[kb][i] = (key >= r_lo && key < r_hi) ? sacc[kb][i] : -INFINITY;
           }
       }
 
       // ---- row maximum (exact, so the reduction order is immaterial) ----
-      float mx = x[0][0];
+      float mx = sacc[0][0];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x[kb][i]);
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if constexpr (MODE == 0) mx = mx * p.scale_log2;  // -inf stays -inf (scale > 0)
       const float m_new = fmaxf(m_run, mx);
       const float shift = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - shift);
@@ -390,7 +339,12 @@ __global__ void __launch_bounds__(NW * 64) fa_fwd_kernel(Params p) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pw[kb][i] = __builtin_amdgcn_exp2f(x[kb][i] - shift);
+        for (int i = 0; i < 16; ++i) {
+          if constexpr (MODE == 0)
+            pw[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], p.scale_log2, -shift));
+          else
+            pw[kb][i] = __builtin_amdgcn_exp2f(sacc[kb][i] - shift);
+        }
       float s8[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
@@ -411,20 +365,38 @@ __global__ void __launch_bounds__(NW * 64) fa_fwd_kernel(Params p) {
       // ---- O^T += V^T P^T ----
       if constexpr (BF16) {
         // MFMA c covers keys 16c..16c+15; lane half h supplies keys 16c + 8(j/4) + 4h + j%4,
-        // which are its S^T registers i = 8(c%2) + j of block c/2.
+        // which are its S^T registers i = 8(c%2) + j of block c/2.  The matching V^T operand
+        // comes from two transposing reads: within each 16-lane group, lane r reads 4 d of
+        // key 16c + 8e + 4h + r/4, and lane i receives key ... + j (j = 0..3) at one d.
         bf16x8 pb[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
           for (int j = 0; j < 8; ++j) pb[c][j] = (__bf16)pw[c >> 1][8 * (c & 1) + j];
+        const int r16 = lane & 15, dh = (lane >> 4) & 1;
+        const int key_l = 4 * half + (r16 >> 2);      // key offset of this lane's read
+        const int d_l = 16 * dh + 4 * (r16 & 3);      // d offset (elements) of this lane's read
+        const uint32_t vbase_l = lds_addr(vl) + key_l * (D * 2) + (d_l & 7) * 2;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int d = db * 32 + lq;
+          const int d = db * 32 + d_l;
+          // the swizzle depends on key % 4 (d = 128) or (key / 2) % 2 (d = 64), i.e. on key_l only
+          const uint32_t a0 = vbase_l + (((d >> 3) ^ L::vsw(key_l)) * 16);
+          s16x4 r[8];  // r[2c + e]: keys 16c + 8e + key_l
+          r[0] = lds_read_tr16<0 * D * 2>(a0);
+          r[1] = lds_read_tr16<8 * D * 2>(a0);
+          r[2] = lds_read_tr16<16 * D * 2>(a0);
+          r[3] = lds_read_tr16<24 * D * 2>(a0);
+          r[4] = lds_read_tr16<32 * D * 2>(a0);
+          r[5] = lds_read_tr16<40 * D * 2>(a0);
+          r[6] = lds_read_tr16<48 * D * 2>(a0);
+          r[7] = lds_read_tr16<56 * D * 2>(a0);
+          lds_wait(r[0], r[1], r[2], r[3], r[4], r[5], r[6], r[7]);
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            const int ch = (2 * c + half) ^ (d & 7);
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vl + d * (kBc * 2) + ch * 16);
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], oacc[db], 0, 0, 0);
+            const s16x8 both = __builtin_shufflevector(r[2 * c], r[2 * c + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb[c],
+                                                               oacc[db], 0, 0, 0);
           }
         }
       } else {
@@ -437,18 +409,26 @@ __global__ void __launch_bounds__(NW * 64) fa_fwd_kernel(Params p) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               const int key = kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-              const float a = *reinterpret_cast<const float *>(vl + (key * D + (d ^ (((key >> 2) & 1) << 5))) * 4);
+              const int ch = (d >> 2) ^ L::vsw(key);
+              const float a = *reinterpret_cast<const float *>(vl + key * (D * 4) + ch * 16 + (d & 3) * 4);
               oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pw[kb][i], oacc[db], 0, 0, 0);
             }
         }
       }
     }
 
-    if (IO::PIPE && t + 1 < t_end) {
-      unsigned char *kn = smem + (buf ^ 1) * 2 * IO::TILE_BYTES;
-      io.store(kn, kn + IO::TILE_BYTES, tid);
-    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile t + 1 have landed
+    __syncthreads();                // ... everyone's have, and buffer `kl` is free again
+  };
+
+  if (t_begin < t_end) {
+    issue_tile(t_begin, smem0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  }
+  for (int t = t_begin; t < t_end; t += 2) {
+    step(t, smem0, smem1);
+    if (t + 1 < t_end) step(t + 1, smem1, smem0);
   }
 
   // ---- epilogue: o = a / l, lse = m + ln l; a row that saw nothing gets 0 and -inf ----
@@ -486,16 +466,16 @@ __global__ void __launch_bounds__(NW * 64) fa_fwd_kernel(Params p) {
 typedef void (*KernelFn)(Params);
 
 template <bool BF16, int D, int NW>
-KernelFn pick_mask(bool mask) {
-  return mask ? fa_fwd_kernel<BF16, D, NW, true> : fa_fwd_kernel<BF16, D, NW, false>;
+KernelFn pick_mode(int mode) {
+  return mode ? fa_fwd_kernel<BF16, D, NW, 1> : fa_fwd_kernel<BF16, D, NW, 0>;
 }
 
 template <bool BF16, int D>
-KernelFn pick_nw(int nw, bool mask) {
+KernelFn pick_nw(int nw, int mode) {
   switch (nw) {
-    case 1: return pick_mask<BF16, D, 1>(mask);
-    case 2: return pick_mask<BF16, D, 2>(mask);
-    default: return pick_mask<BF16, D, 4>(mask);
+    case 1: return pick_mode<BF16, D, 1>(mode);
+    case 2: return pick_mode<BF16, D, 2>(mode);
+    default: return pick_mode<BF16, D, 4>(mode);
   }
 }
 
@@ -607,9 +587,11 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   p.scale_log2 = scale * kLog2e;
 
   const bool bf16 = dtype == FA_BF16;
-  const bool has_mask = mask != nullptr;
-  KernelFn fn = bf16 ? (d == 64 ? pick_nw<true, 64>(nw, has_mask) : pick_nw<true, 128>(nw, has_mask))
-                     : (d == 64 ? pick_nw<false, 64>(nw, has_mask) : pick_nw<false, 128>(nw, has_mask));
+  // MODE 1 when scores need the explicit form: an additive mask, or a scale that is not
+  // positive (the raw-maximum shortcut needs scale > 0).
+  const int mode = (mask != nullptr || !(scale > 0.f)) ? 1 : 0;
+  KernelFn fn = bf16 ? (d == 64 ? pick_nw<true, 64>(nw, mode) : pick_nw<true, 128>(nw, mode))
+                     : (d == 64 ? pick_nw<false, 64>(nw, mode) : pick_nw<false, 128>(nw, mode));
   (void)hipGetLastError();  // clear a stale error so the check below reports this launch
   hipLaunchKernelGGL(fn, dim3((unsigned)n_blocks), dim3(nw * 64), 0,
                      static_cast<hipStream_t>(stream), p);
