@@ -48,6 +48,7 @@ constexpr int kBc = 64;       // keys per tile
 constexpr int kRowsWave = 32; // query rows per wave (N of the 32x32 MFMA)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.f;  // base-2 headroom before the running maximum is moved
 
 struct Params {
   const void *q, *k, *v;
@@ -93,9 +94,9 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 }
 
 // ---------------------------------------------------------------------------------------
-// K/V tiles go from HBM straight into LDS (global_load_lds, 16 bytes per lane: lane l of
-// the wave writes bytes [16 l, 16 l + 16) of a 1 KiB LDS block), so no registers hold them
-// and nothing is transposed on the way.  Both tiles are row-major [64 keys][D] in LDS with
+// K/V tiles go from HBM straight into LDS (buffer loads that write LDS, 16 bytes per lane:
+// lane l of the wave writes bytes [16 l, 16 l + 16) of a 1 KiB LDS block), so no registers
+// hold them and nothing is transposed on the way.  Both tiles are row-major [64 keys][D] in LDS with
 // the 16-byte chunks of each row XOR-swizzled so that the MFMA operand reads are spread
 // over the LDS banks:
 //   K (read 16 bytes per lane, 32 rows at a time): chunk ^ (key % min(chunks per row, 16)).
@@ -103,17 +104,12 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 //     for d = 128, chunk ^ 4 ((key / 2) % 2) for d = 64.
 //   fp32 V (read 4 bytes per lane; the two lane halves read keys 4 apart): chunk ^ 8 * bit 2
 //     of the key.
-// Rows past Tk are loaded from row Tk - 1 (real, finite data): their scores are replaced by
-// -inf and their weights are 0, so they add nothing.
+// Rows past Tk read as zeros: their scores are replaced by -inf and their weights are 0.
 // ---------------------------------------------------------------------------------------
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ void g2l16(const unsigned char *g, unsigned char *lds_block) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
-                                   (__attribute__((address_space(3))) void *)lds_block, 16, 0, 0);
-}
 
 // ds_read_b64_tr_b16 at LDS byte address `addr`.  Within each group of 16 lanes, lane r
 // supplies 4 consecutive 16-bit elements; lane i receives element i % 4 of the chunks of lanes
@@ -127,11 +123,32 @@ __device__ __forceinline__ s16x4 lds_read_tr16(uint32_t addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFFSET));
   return r;
 }
-// Waits for every outstanding LDS read of this wave; the operands tie the wait to the values
-// it guards, so their uses cannot move above it.
-__device__ __forceinline__ void lds_wait(s16x4 &a, s16x4 &b, s16x4 &c, s16x4 &d, s16x4 &e, s16x4 &f,
-                                         s16x4 &g, s16x4 &h) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h));
+// ds_read_b128 at LDS byte address `addr` + OFFSET, issued as inline assembly like the
+// transposing read (the wait is placed by the caller).
+template <int OFFSET>
+__device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
+  static_assert(OFFSET >= 0 && OFFSET < 65536, "ds offset field is 16 bits");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFFSET));
+  return r;
+}
+// Waits until at most N of this wave's LDS reads are outstanding.  LDS reads complete in
+// order and these code paths issue no scalar-memory reads, so all but the N newest reads have
+// landed.  The operands tie the wait to the values it guards, so their uses cannot move
+// above it.
+template <int N, typename T>
+__device__ __forceinline__ void lds_wait(T &a, T &b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
+}
+template <int N, typename T>
+__device__ __forceinline__ void lds_wait(T &a, T &b, T &c, T &d) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "i"(N));
+}
+template <int N, typename T>
+__device__ __forceinline__ void lds_wait(T &a, T &b, T &c, T &d, T &e, T &f, T &g, T &h) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h)
+               : "i"(N));
 }
 __device__ __forceinline__ uint32_t lds_addr(const unsigned char *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)p;
@@ -152,288 +169,327 @@ struct Layout {
   }
 };
 
-template <bool BF16, int D, int NW, int MODE>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 1)))
-fa_fwd_kernel(Params p) {
-  using L = Layout<BF16, D>;
-  constexpr int ES = L::ES;
-  constexpr int NDB = D / 32;  // 32-row blocks of O^T
-  constexpr int BPW = L::NBLK / NW;  // 1 KiB blocks each wave copies per tensor per tile
-  static_assert(L::NBLK % NW == 0, "blocks per tile must split evenly over the waves");
-  // Two LDS buffers as two objects (each [K | V]), so that the compiler can tell the copy into
-  // one from the reads of the other and does not wait for the copy before those reads.
-  __shared__ __attribute__((aligned(1024))) unsigned char smem0[2 * L::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char smem1[2 * L::TILE_BYTES];
-
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int half = lane >> 5, lq = lane & 31;
-
-  // ---- work decode: (b, kv head, row tile, head group) ----
-  const int w = xcd_remap(blockIdx.x, p.n_blocks);
-  const int hg = w % p.n_head_groups;
-  int rest = w / p.n_head_groups;
-  const int rti = rest % p.n_row_tiles;
-  rest /= p.n_row_tiles;
-  const int kvh = rest % p.Hkv;
-  const int b = rest / p.Hkv;
-  const int rt = p.causal ? p.n_row_tiles - 1 - rti : rti;  // heavy (late) row tiles first
-
-  const int G = p.heads_per_block;
-  const int head = kvh * p.group + hg * G + (wid % G);
-  const int row0_blk = rt * p.rows_per_block;
-  const int row0_wave = row0_blk + (wid / G) * kRowsWave;
-  const int row = row0_wave + lq;
-  const bool row_ok = row < p.Tq;
-
-  // ---- key-tile ranges ----
-  int t_begin = 0, t_end = 0;  // workgroup: union of its rows' visible tiles
-  {
+// ---------------------------------------------------------------------------------------
+// Work decode and the key-tile ranges of one workgroup.
+// ---------------------------------------------------------------------------------------
+struct Work {
+  int b, kvh, head_base, row0_blk, t_begin, t_end;
+  __device__ __forceinline__ Work(const Params &p) {
+    const int w = xcd_remap(blockIdx.x, p.n_blocks);
+    const int hg = w % p.n_head_groups;
+    int rest = w / p.n_head_groups;
+    const int rti = rest % p.n_row_tiles;
+    rest /= p.n_row_tiles;
+    kvh = rest % p.Hkv;
+    b = rest / p.Hkv;
+    const int rt = p.causal ? p.n_row_tiles - 1 - rti : rti;  // heavy (late) row tiles first
+    head_base = kvh * p.group + hg * p.heads_per_block;
+    row0_blk = rt * p.rows_per_block;
+    // the union of the visible tiles of the workgroup's rows (lo and hi grow with the position)
+    t_begin = t_end = 0;
     const int last = min(row0_blk + p.rows_per_block, p.Tq) - 1;
     const int64_t lo = vis_lo(p.q_offset + row0_blk, p), hi = vis_hi(p.q_offset + last, p);
     if (hi > lo) { t_begin = (int)(lo / kBc); t_end = (int)((hi + kBc - 1) / kBc); }
   }
-  int w_begin = 0, w_end = 0;        // this wave's visible tiles
-  int64_t full_lo = 1, full_hi = 0;  // tiles inside [full_lo, full_hi) are visible to all its rows
-  if (row0_wave < p.Tq) {
-    const int last = min(row0_wave + kRowsWave, p.Tq) - 1;
-    const int64_t lo0 = vis_lo(p.q_offset + row0_wave, p), hi1 = vis_hi(p.q_offset + last, p);
-    if (hi1 > lo0) { w_begin = (int)(lo0 / kBc); w_end = (int)((hi1 + kBc - 1) / kBc); }
-    full_lo = vis_lo(p.q_offset + last, p);
-    full_hi = vis_hi(p.q_offset + row0_wave, p);
-  }
-  const int64_t r_lo = row_ok ? vis_lo(p.q_offset + row, p) : 0;
-  const int64_t r_hi = row_ok ? vis_hi(p.q_offset + row, p) : 0;
+};
 
-  // ---- Q of this lane's row, held in registers as the MFMA B operand ----
-  const unsigned char *qrow = static_cast<const unsigned char *>(p.q) +
-                              ((int64_t)b * p.sq_b + (int64_t)head * p.sq_h + (int64_t)row * p.sq_t) * ES;
+// ---------------------------------------------------------------------------------------
+// One wave: 32 query rows of one head.  Holds the rows' Q (MFMA B operand), the O^T
+// accumulators and the online-softmax state, and does the per-tile math.
+// ---------------------------------------------------------------------------------------
+template <bool BF16, int D, int MODE>
+struct Wave {
+  using L = Layout<BF16, D>;
+  static constexpr int ES = L::ES;
+  static constexpr int NDB = D / 32;  // 32-row blocks of O^T
+
+  int half, lq, lane, row;
+  bool row_ok;
+  int r_lo, r_hi;            // this row's visible keys [r_lo, r_hi)
+  int w_begin, w_end;        // tiles holding any key visible to the wave's rows
+  int64_t full_lo, full_hi;  // tiles inside [full_lo, full_hi) are visible to all its rows
+  const float *mrow;
   bf16x8 qb[BF16 ? D / 16 : 1];
   float qf[BF16 ? 1 : D / 2];
-  if constexpr (BF16) {
-#pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (row_ok) val = *reinterpret_cast<const u32x4 *>(qrow + (ds * 16 + 8 * half) * 2);
-      qb[ds] = __builtin_bit_cast(bf16x8, val);
-    }
-  } else {
-    // the two lane halves split d: half h owns d in [h * D/2, (h + 1) * D/2)
-#pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-      f32x4 val = {0.f, 0.f, 0.f, 0.f};
-      if (row_ok) val = *reinterpret_cast<const f32x4 *>(qrow + (half * (D / 2) + 4 * c) * 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qf[4 * c + e] = val[e];
-    }
-  }
-
-  // ---- online-softmax state: m (base-2 units), this half's partial l, O^T accumulators ----
-  float m_run = -INFINITY, l_run = 0.f;
-  if (p.sinks) {  // a sink is the first "tile": m = z_h, l = e^0 = 1, a = 0
-    m_run = p.sinks[head] * kLog2e;
-    l_run = half == 0 ? 1.f : 0.f;
-  }
+  float m_run, l_run;        // reference maximum (base-2 units) and this half's partial l
   f32x16 oacc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  f32x16 sacc[2];            // S^T of the current tile; lane holds key 32kb + 8(i/4) + 4 half + i%4
+  bf16x8 pb[BF16 ? 4 : 1];   // bf16 weights, the B operand of the PV MFMAs
+  float pw[BF16 ? 1 : 2][16];  // fp32 weights (fp32 path)
 
-  const unsigned char *kbase = static_cast<const unsigned char *>(p.k) +
-                               ((int64_t)b * p.sk_b + (int64_t)kvh * p.sk_h) * ES;
-  const unsigned char *vbase = static_cast<const unsigned char *>(p.v) +
-                               ((int64_t)b * p.sv_b + (int64_t)kvh * p.sv_h) * ES;
-  const float *mrow = MODE == 1 && p.mask
-                          ? p.mask + (int64_t)b * p.sm_b + (int64_t)head * p.sm_h + (int64_t)row * p.sm_i
-                          : nullptr;
-
-  // This lane's part of the tile copy: row (block * RB + lane / CH), stored chunk lane % CH.
-  const int cp_row = lane / L::CH, cp_chunk = lane % L::CH;
-  auto issue_tile = [&](int t, unsigned char *kl) {
-    unsigned char *vl = kl + L::TILE_BYTES;
-#pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      const int blk = wid * BPW + i;
-      const int r = blk * L::RB + cp_row;
-      int key = t * kBc + r;
-      key = key < p.Tk ? key : p.Tk - 1;
-      g2l16(kbase + (int64_t)key * p.sk_t * ES + ((cp_chunk ^ L::ksw(r)) * 16), kl + blk * 1024);
-      g2l16(vbase + (int64_t)key * p.sv_t * ES + ((cp_chunk ^ L::vsw(r)) * 16), vl + blk * 1024);
+  __device__ __forceinline__ void init(const Params &p, int b, int head, int row0_wave, int lane_) {
+    lane = lane_;
+    half = lane >> 5;
+    lq = lane & 31;
+    row = row0_wave + lq;
+    row_ok = row < p.Tq;
+    w_begin = w_end = 0;
+    full_lo = 1;
+    full_hi = 0;
+    if (row0_wave < p.Tq) {
+      const int last = min(row0_wave + kRowsWave, p.Tq) - 1;
+      const int64_t lo0 = vis_lo(p.q_offset + row0_wave, p), hi1 = vis_hi(p.q_offset + last, p);
+      if (hi1 > lo0) { w_begin = (int)(lo0 / kBc); w_end = (int)((hi1 + kBc - 1) / kBc); }
+      full_lo = vis_lo(p.q_offset + last, p);
+      full_hi = vis_hi(p.q_offset + row0_wave, p);
     }
-  };
+    // clamped to [0, Tk] so they fit 32 bits
+    r_hi = row_ok ? (int)vis_hi(p.q_offset + row, p) : 0;
+    r_lo = row_ok ? (int)min(vis_lo(p.q_offset + row, p), (int64_t)r_hi) : 0;
+    mrow = MODE == 1 && p.mask
+               ? p.mask + (int64_t)b * p.sm_b + (int64_t)head * p.sm_h + (int64_t)row * p.sm_i
+               : nullptr;
 
-  // One tile of work: wait-free reads of `kl` (tile t), copy of tile t + 1 into `kn`.
-  auto step = [&](int t, const unsigned char *kl, unsigned char *kn) {
-    const unsigned char *vl = kl + L::TILE_BYTES;
-    if (t + 1 < t_end) issue_tile(t + 1, kn);  // that buffer was released by the last barrier
+    const unsigned char *qrow = static_cast<const unsigned char *>(p.q) +
+                                ((int64_t)b * p.sq_b + (int64_t)head * p.sq_h + (int64_t)row * p.sq_t) * ES;
+    if constexpr (BF16) {
+#pragma unroll
+      for (int ds = 0; ds < D / 16; ++ds) {
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (row_ok) val = *reinterpret_cast<const u32x4 *>(qrow + (ds * 16 + 8 * half) * 2);
+        qb[ds] = __builtin_bit_cast(bf16x8, val);
+      }
+    } else {
+      // the two lane halves split d: half h owns d in [h * D/2, (h + 1) * D/2)
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) {
+        f32x4 val = {0.f, 0.f, 0.f, 0.f};
+        if (row_ok) val = *reinterpret_cast<const f32x4 *>(qrow + (half * (D / 2) + 4 * c) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qf[4 * c + e] = val[e];
+      }
+    }
+    m_run = -INFINITY;
+    l_run = 0.f;
+    if (p.sinks) {  // a sink is the first "tile": m = z_h, l = e^0 = 1, a = 0
+      m_run = p.sinks[head] * kLog2e;
+      l_run = half == 0 ? 1.f : 0.f;
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  }
 
-    if (t >= w_begin && t < w_end) {
-      // ---- S^T = K Q^T for two 32-key blocks; lane holds key 32kb + 8(i/4) + 4 half + i%4 ----
-      f32x16 sacc[2];
+  __device__ __forceinline__ bool active(int t) const { return t >= w_begin && t < w_end; }
+
+  // S^T = K Q^T for the two 32-key blocks of the tile in `kl`.  The two blocks' MFMA chains
+  // are interleaved so that consecutive MFMAs are independent.
+  __device__ __forceinline__ void qk(const unsigned char *kl) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 acc;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-        const int key = kb * 32 + lq;
-        if constexpr (BF16) {
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+    if constexpr (BF16) {
+      // K operand of step ds for both key blocks: row kb * 32 + lq, chunk (2 ds + half) swizzled
+      // by the row (key % chunks-per-row is lq % chunks-per-row for both blocks).  The reads
+      // for step ds + 1 are in flight while the MFMAs of step ds run.
+      constexpr int NDS = D / 16;
+      const uint32_t krow = lds_addr(kl) + lq * (D * 2);
+      const int m = L::ksw(lq);
+      u32x4 ka[2][2];
+      auto issue = [&](int ds) {
+        const uint32_t a = krow + ((((2 * ds + half) ^ m)) << 4);
+        ka[ds & 1][0] = lds_read_b128<0>(a);
+        ka[ds & 1][1] = lds_read_b128<32 * D * 2>(a);
+      };
+      issue(0);
 #pragma unroll
-          for (int ds = 0; ds < D / 16; ++ds) {
-            const int ch = (2 * ds + half) ^ L::ksw(key);
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kl + key * (D * 2) + ch * 16);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ds], acc, 0, 0, 0);
-          }
+      for (int ds = 0; ds < NDS; ++ds) {
+        if (ds + 1 < NDS) {
+          issue(ds + 1);
+          lds_wait<2>(ka[ds & 1][0], ka[ds & 1][1]);
         } else {
-#pragma unroll
-          for (int c = 0; c < D / 8; ++c) {
-            const int ch = (half * (D / 8) + c) ^ L::ksw(key);
-            const f32x4 a4 = *reinterpret_cast<const f32x4 *>(kl + key * (D * 4) + ch * 16);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[e], qf[4 * c + e], acc, 0, 0, 0);
-          }
+          lds_wait<0>(ka[ds & 1][0], ka[ds & 1][1]);
         }
-        sacc[kb] = acc;
-      }
-
-      // ---- scores; keys a row cannot see become -inf by select ----
-      // MODE 0 (no mask, scale > 0): the row maximum is taken on the raw dot products (scaling
-      //   by a positive constant commutes with max and with fp32 rounding), and each weight is
-      //   exp2(fma(s, scale log2 e, -m)).
-      // MODE 1 (additive mask, or scale <= 0): x = fma(s, scale log2 e, mask log2 e) first.
-      const bool full = (int64_t)t * kBc >= full_lo && (int64_t)t * kBc + kBc <= full_hi;
-      if constexpr (MODE == 1) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = t * kBc + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-            const float mv = (mrow && row_ok && key < p.Tk) ? mrow[(int64_t)key * p.sm_j] : 0.f;
-            sacc[kb][i] = __builtin_fmaf(sacc[kb][i], p.scale_log2, mv * kLog2e);
-          }
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[ds & 1][kb]),
+                                                             qb[ds], sacc[kb], 0, 0, 0);
       }
-      if (!full) {
+    } else {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int c = 0; c < D / 8; ++c) {
+        f32x4 a4[2];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int64_t key = (int64_t)t * kBc + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-            sacc[kb][i] = (key >= r_lo && key < r_hi) ? sacc[kb][i] : -INFINITY;
-          }
+        for (int kb = 0; kb < 2; ++kb) {
+          const int key = kb * 32 + lq;
+          const int ch = (half * (D / 8) + c) ^ L::ksw(key);
+          a4[kb] = *reinterpret_cast<const f32x4 *>(kl + key * (D * 4) + ch * 16);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[kb][e], qf[4 * c + e], sacc[kb], 0, 0, 0);
       }
+    }
+  }
 
-      // ---- row maximum (exact, so the reduction order is immaterial) ----
-      float mx = sacc[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if constexpr (MODE == 0) mx = mx * p.scale_log2;  // -inf stays -inf (scale > 0)
-      const float m_new = fmaxf(m_run, mx);
-      const float shift = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - shift);
-
-      // ---- weights and this half's partial denominator (fixed pairwise tree) ----
-      float pw[2][16];
+  // Online-softmax step for tile t: scores -> weights, running maximum and denominator, and
+  // the rescale of O^T.
+  __device__ __forceinline__ void softmax(const Params &p, int t) {
+    // MODE 0 (no mask, scale > 0): the row maximum is taken on the raw dot products (scaling
+    //   by a positive constant commutes with max and with fp32 rounding), and each weight is
+    //   exp2(fma(s, scale log2 e, -m)).
+    // MODE 1 (additive mask, or scale <= 0): x = fma(s, scale log2 e, mask log2 e) first.
+    const bool full = (int64_t)t * kBc >= full_lo && (int64_t)t * kBc + kBc <= full_hi;
+    if constexpr (MODE == 1) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          if constexpr (MODE == 0)
-            pw[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], p.scale_log2, -shift));
-          else
-            pw[kb][i] = __builtin_amdgcn_exp2f(sacc[kb][i] - shift);
+          const int key = t * kBc + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+          const float mv = (mrow && row_ok && key < p.Tk) ? mrow[(int64_t)key * p.sm_j] : 0.f;
+          sacc[kb][i] = __builtin_fmaf(sacc[kb][i], p.scale_log2, mv * kLog2e);
         }
-      float s8[8];
+    }
+    if (!full) {  // keys this row cannot see become -inf by select
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        s8[j] = (pw[j >> 2][4 * (j & 3)] + pw[j >> 2][4 * (j & 3) + 1]) +
-                (pw[j >> 2][4 * (j & 3) + 2] + pw[j >> 2][4 * (j & 3) + 3]);
-      const float lsum = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
-      l_run = __builtin_fmaf(alpha, l_run, lsum);
-      m_run = m_new;
-
-      // ---- rescale O^T (skipped when alpha == 1 in every lane: multiplying by 1 is exact) ----
-      if (__ballot(alpha != 1.f)) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      }
-
-      // ---- O^T += V^T P^T ----
-      if constexpr (BF16) {
-        // MFMA c covers keys 16c..16c+15; lane half h supplies keys 16c + 8(j/4) + 4h + j%4,
-        // which are its S^T registers i = 8(c%2) + j of block c/2.  The matching V^T operand
-        // comes from two transposing reads: within each 16-lane group, lane r reads 4 d of
-        // key 16c + 8e + 4h + r/4, and lane i receives key ... + j (j = 0..3) at one d.
-        bf16x8 pb[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) pb[c][j] = (__bf16)pw[c >> 1][8 * (c & 1) + j];
-        const int r16 = lane & 15, dh = (lane >> 4) & 1;
-        const int key_l = 4 * half + (r16 >> 2);      // key offset of this lane's read
-        const int d_l = 16 * dh + 4 * (r16 & 3);      // d offset (elements) of this lane's read
-        const uint32_t vbase_l = lds_addr(vl) + key_l * (D * 2) + (d_l & 7) * 2;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int d = db * 32 + d_l;
-          // the swizzle depends on key % 4 (d = 128) or (key / 2) % 2 (d = 64), i.e. on key_l only
-          const uint32_t a0 = vbase_l + (((d >> 3) ^ L::vsw(key_l)) * 16);
-          s16x4 r[8];  // r[2c + e]: keys 16c + 8e + key_l
-          r[0] = lds_read_tr16<0 * D * 2>(a0);
-          r[1] = lds_read_tr16<8 * D * 2>(a0);
-          r[2] = lds_read_tr16<16 * D * 2>(a0);
-          r[3] = lds_read_tr16<24 * D * 2>(a0);
-          r[4] = lds_read_tr16<32 * D * 2>(a0);
-          r[5] = lds_read_tr16<40 * D * 2>(a0);
-          r[6] = lds_read_tr16<48 * D * 2>(a0);
-          r[7] = lds_read_tr16<56 * D * 2>(a0);
-          lds_wait(r[0], r[1], r[2], r[3], r[4], r[5], r[6], r[7]);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const s16x8 both = __builtin_shufflevector(r[2 * c], r[2 * c + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb[c],
-                                                               oacc[db], 0, 0, 0);
-          }
+        for (int i = 0; i < 16; ++i) {
+          const int key = t * kBc + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+          sacc[kb][i] = (key >= r_lo && key < r_hi) ? sacc[kb][i] : -INFINITY;
         }
-      } else {
-        // MFMA (kb, i) contracts 2 keys: lane half h supplies key 32kb + 8(i/4) + 4h + i%4.
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int d = db * 32 + lq;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-              const int ch = (d >> 2) ^ L::vsw(key);
-              const float a = *reinterpret_cast<const float *>(vl + key * (D * 4) + ch * 16 + (d & 3) * 4);
-              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pw[kb][i], oacc[db], 0, 0, 0);
-            }
-        }
-      }
     }
 
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile t + 1 have landed
-    __syncthreads();                // ... everyone's have, and buffer `kl` is free again
-  };
+    // row maximum (exact, so the reduction order is immaterial)
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if constexpr (MODE == 0) mx = mx * p.scale_log2;  // -inf stays -inf (scale > 0)
+    // The reference point m moves only when this tile's maximum exceeds it by more than
+    // kLazy (base-2 units), or m is still -inf: weights are then exp2(x - m) <= 2^kLazy, and
+    // most tiles need no rescale.  The rule depends on the row's own scores only, so a row's
+    // bits stay independent of chunking and query tiling.
+    const float m_new = (mx > m_run + kLazy) ? mx : m_run;
+    const float shift = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - shift);
 
-  if (t_begin < t_end) {
-    issue_tile(t_begin, smem0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-  for (int t = t_begin; t < t_end; t += 2) {
-    step(t, smem0, smem1);
-    if (t + 1 < t_end) step(t + 1, smem1, smem0);
+    // weights and this half's partial denominator (fixed pairwise tree)
+    float w[2][16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if constexpr (MODE == 0)
+          w[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], p.scale_log2, -shift));
+        else
+          w[kb][i] = __builtin_amdgcn_exp2f(sacc[kb][i] - shift);
+      }
+    float s8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      s8[j] = (w[j >> 2][4 * (j & 3)] + w[j >> 2][4 * (j & 3) + 1]) +
+              (w[j >> 2][4 * (j & 3) + 2] + w[j >> 2][4 * (j & 3) + 3]);
+    const float lsum = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+    l_run = __builtin_fmaf(alpha, l_run, lsum);
+    m_run = m_new;
+
+    if constexpr (BF16) {
+      // MFMA c covers keys 16c..16c+15; lane half h supplies keys 16c + 8(j/4) + 4h + j%4,
+      // which are its S^T registers i = 8(c%2) + j of block c/2.
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pb[c][j] = (__bf16)w[c >> 1][8 * (c & 1) + j];
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pw[kb][i] = w[kb][i];
+    }
+
+    // rescale O^T (skipped when alpha == 1 in every lane: multiplying by 1 is exact)
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
   }
 
-  // ---- epilogue: o = a / l, lse = m + ln l; a row that saw nothing gets 0 and -inf ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (row_ok) {
+  // O^T += V^T P^T with the tile's V in `vl`.  The MFMAs are ordered key block outer, d block
+  // inner, so that consecutive MFMAs accumulate into different registers.
+  __device__ __forceinline__ void pv(const unsigned char *vl) {
+    if constexpr (BF16) {
+      // The V^T operand of MFMA c comes from two transposing reads: within each 16-lane group,
+      // lane r reads 4 d of key 16c + 8e + 4h + r/4, and lane i receives keys ... + j
+      // (j = 0..3) at one d.
+      const int r16 = lane & 15, dh = (lane >> 4) & 1;
+      const int key_l = 4 * half + (r16 >> 2);  // key offset of this lane's read
+      const int d_l = 16 * dh + 4 * (r16 & 3);  // d offset (elements) of this lane's read
+      const uint32_t vbase_l = lds_addr(vl) + key_l * (D * 2) + (d_l & 7) * 2;
+      // the swizzle depends on key % 4 (d = 128) or (key / 2) % 2 (d = 64), i.e. on key_l only
+      uint32_t a0[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) a0[db] = vbase_l + ((((db * 32 + d_l) >> 3) ^ L::vsw(key_l)) * 16);
+      s16x4 r[2][8];  // r[c & 1][2 db + e]: keys 16c + 8e + key_l of d block db
+      auto issue = [&](int c) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          r[c & 1][2 * db] = read_v(a0[db], c, 0);
+          r[c & 1][2 * db + 1] = read_v(a0[db], c, 1);
+        }
+      };
+      issue(0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        s16x4 *rc = r[c & 1];
+        if (c + 1 < 4) {  // the reads for key block c + 1 are in flight during the MFMAs of c
+          issue(c + 1);
+          if constexpr (NDB == 4) lds_wait<8>(rc[0], rc[1], rc[2], rc[3], rc[4], rc[5], rc[6], rc[7]);
+          else lds_wait<4>(rc[0], rc[1], rc[2], rc[3]);
+        } else {
+          if constexpr (NDB == 4) lds_wait<0>(rc[0], rc[1], rc[2], rc[3], rc[4], rc[5], rc[6], rc[7]);
+          else lds_wait<0>(rc[0], rc[1], rc[2], rc[3]);
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const s16x8 both = __builtin_shufflevector(rc[2 * db], rc[2 * db + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb[c],
+                                                             oacc[db], 0, 0, 0);
+        }
+      }
+    } else {
+      // MFMA (kb, i) contracts 2 keys: lane half h supplies key 32kb + 8(i/4) + 4h + i%4.
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const int d = db * 32 + lq;
+            const int ch = (d >> 2) ^ L::vsw(key);
+            const float a = *reinterpret_cast<const float *>(vl + key * (D * 4) + ch * 16 + (d & 3) * 4);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pw[kb][i], oacc[db], 0, 0, 0);
+          }
+        }
+    }
+  }
+  // transposing read of keys 16c + 8e + key_l (immediate offset), see pv()
+  __device__ __forceinline__ static s16x4 read_v(uint32_t a, int c, int e) {
+    switch (2 * c + e) {
+      case 0: return lds_read_tr16<0 * D * 2>(a);
+      case 1: return lds_read_tr16<8 * D * 2>(a);
+      case 2: return lds_read_tr16<16 * D * 2>(a);
+      case 3: return lds_read_tr16<24 * D * 2>(a);
+      case 4: return lds_read_tr16<32 * D * 2>(a);
+      case 5: return lds_read_tr16<40 * D * 2>(a);
+      case 6: return lds_read_tr16<48 * D * 2>(a);
+      default: return lds_read_tr16<56 * D * 2>(a);
+    }
+  }
+
+  // o = a / l, lse = m + ln l; a row that saw nothing gets 0 and -inf.
+  __device__ __forceinline__ void finish(const Params &p, int b, int head) {
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (!row_ok) return;
     unsigned char *orow = static_cast<unsigned char *>(p.o) +
                           ((int64_t)b * p.so_b + (int64_t)head * p.so_h + (int64_t)row * p.so_t) * ES;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -457,6 +513,177 @@ fa_fwd_kernel(Params p) {
       p.lse[(int64_t)b * p.sl_b + (int64_t)head * p.sl_h + row] =
           l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   }
+};
+
+// ---------------------------------------------------------------------------------------
+// The tile copy HBM -> LDS, split over the NW waves of the workgroup, as buffer loads that
+// write LDS directly (buffer_load_dwordx4 ... lds: lane l of a wave writes bytes
+// [16 l, 16 l + 16) of a 1 KiB LDS block).  The buffer resource covers the tile and the rest
+// of the (b, KV head) slice; lane l copies row (blk * RB + l / CH), stored chunk l % CH, of its
+// blocks at a fixed 32-bit offset.  Reads past the end of the slice (rows past Tk) return
+// zeros.  The host checks that a slice spans less than 2 GiB.
+// ---------------------------------------------------------------------------------------
+template <bool BF16, int D, int NW>
+struct Copier {
+  using L = Layout<BF16, D>;
+  static constexpr int ES = L::ES;
+  static constexpr int BPW = L::NBLK / NW;  // 1 KiB blocks each wave copies per tensor per tile
+  static_assert(L::NBLK % NW == 0, "blocks per tile must split evenly over the waves");
+  const unsigned char *kbase, *vbase;
+  int64_t kbytes, vbytes;  // bytes of each slice from its first key to the end of key Tk - 1
+  int wid;
+  uint32_t koff[BPW], voff[BPW];
+
+  __device__ __forceinline__ void init(const Params &p, int b, int kvh, int wid_, int lane) {
+    wid = wid_;
+    kbase = static_cast<const unsigned char *>(p.k) + ((int64_t)b * p.sk_b + (int64_t)kvh * p.sk_h) * ES;
+    vbase = static_cast<const unsigned char *>(p.v) + ((int64_t)b * p.sv_b + (int64_t)kvh * p.sv_h) * ES;
+    kbytes = ((int64_t)(p.Tk - 1) * p.sk_t + D) * ES;
+    vbytes = ((int64_t)(p.Tk - 1) * p.sv_t + D) * ES;
+    const int cp_row = lane / L::CH, cp_chunk = lane % L::CH;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int r = (wid * BPW + i) * L::RB + cp_row;
+      koff[i] = (uint32_t)(r * p.sk_t * ES) + ((cp_chunk ^ L::ksw(r)) * 16);
+      voff[i] = (uint32_t)(r * p.sv_t * ES) + ((cp_chunk ^ L::vsw(r)) * 16);
+    }
+  }
+  template <bool IS_K>
+  __device__ __forceinline__ void tile(const Params &p, int t, unsigned char *dst) const {
+#if defined(__HIP_DEVICE_COMPILE__)  // the buffer builtins exist in the device pass only
+    const int64_t skip = (int64_t)t * kBc * (IS_K ? p.sk_t : p.sv_t) * ES;
+    const int64_t left = (IS_K ? kbytes : vbytes) - skip;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((IS_K ? kbase : vbase) + skip), (short)0, (int)(left < INT32_MAX ? left : INT32_MAX),
+        0x00020000 /* raw dwords */);
+#pragma unroll
+    for (int i = 0; i < BPW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void *)(dst + (wid * BPW + i) * 1024), 16,
+          IS_K ? koff[i] : voff[i], 0, 0, 0);
+#endif
+  }
+};
+
+// A workgroup-wide barrier that publishes nothing: emitted as a bare s_barrier (the memory
+// clobber keeps the compiler from moving memory accesses across it).
+__device__ __forceinline__ void phase_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// ---------------------------------------------------------------------------------------
+// Streaming kernel (1, 2 or 4 waves): each wave walks the tiles; the next tile is copied
+// into the other LDS buffer while the current one is used.
+// ---------------------------------------------------------------------------------------
+template <bool BF16, int D, int NW, int MODE>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 1)))
+fa_fwd_kernel(Params p) {
+  using L = Layout<BF16, D>;
+  // Two LDS buffers as two objects (each [K | V]), so that the compiler can tell the copy into
+  // one from the reads of the other and does not wait for the copy before those reads.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem0[2 * L::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem1[2 * L::TILE_BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const Work wk(p);
+  const int G = p.heads_per_block;
+  const int head = wk.head_base + wid % G;
+  Wave<BF16, D, MODE> wv;
+  wv.init(p, wk.b, head, wk.row0_blk + (wid / G) * kRowsWave, lane);
+  Copier<BF16, D, NW> cp;
+  cp.init(p, wk.b, wk.kvh, wid, lane);
+
+  auto step = [&](int t, const unsigned char *kl, unsigned char *kn) {
+    if (t + 1 < wk.t_end) {  // that buffer was released by the last barrier
+      cp.template tile<true>(p, t + 1, kn);
+      cp.template tile<false>(p, t + 1, kn + L::TILE_BYTES);
+    }
+    if (wv.active(t)) {
+      wv.qk(kl);
+      wv.softmax(p, t);
+      wv.pv(kl + L::TILE_BYTES);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile t + 1 have landed
+    __syncthreads();                // ... everyone's have, and buffer `kl` is free again
+  };
+  if (wk.t_begin < wk.t_end) {
+    cp.template tile<true>(p, wk.t_begin, smem0);
+    cp.template tile<false>(p, wk.t_begin, smem0 + L::TILE_BYTES);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  for (int t = wk.t_begin; t < wk.t_end; t += 2) {
+    step(t, smem0, smem1);
+    if (t + 1 < wk.t_end) step(t + 1, smem1, smem0);
+  }
+  wv.finish(p, wk.b, head);
+}
+
+// ---------------------------------------------------------------------------------------
+// Ping-pong kernel (8 waves, bf16): waves 0-3 (group A) and 4-7 (group B) sit on the same
+// four SIMDs.  Time is cut into phases separated by workgroup barriers; in each phase one
+// group runs its MFMA work (PV of tile j-1, then QK of tile j) while the other runs its VALU
+// work (the softmax of a tile), and the roles swap every phase, so each SIMD always has one
+// wave feeding the matrix cores and one on the vector ALUs.  Group B runs one phase behind
+// group A.  K runs one tile ahead of V: in phase 2j the copies of K(j+1) and V(j) start
+// (into the buffers last read in phase 2j-1), and they are waited for at the end of phase
+// 2j+1.  Each row's arithmetic is exactly that of the streaming kernel.
+// ---------------------------------------------------------------------------------------
+template <bool BF16, int D, int MODE>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+fa_fwd_pingpong(Params p) {
+  using L = Layout<BF16, D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char k0[L::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char k1[L::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char v0[L::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char v1[L::TILE_BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const bool group_a = wid < 4;
+  const Work wk(p);
+  const int G = p.heads_per_block;
+  const int head = wk.head_base + wid % G;
+  Wave<BF16, D, MODE> wv;
+  wv.init(p, wk.b, head, wk.row0_blk + (wid / G) * kRowsWave, lane);
+  Copier<BF16, D, 8> cp;
+  cp.init(p, wk.b, wk.kvh, wid, lane);
+
+  const int t0 = wk.t_begin, n = wk.t_end - wk.t_begin;
+  // MFMA phase of tile j: PV(j - 1) with V of tile j - 1, QK(j) with K of tile j.
+  auto mfma = [&](int j, const unsigned char *vprev, const unsigned char *kcur) {
+    if (j >= 1 && j - 1 < n && wv.active(t0 + j - 1)) wv.pv(vprev);
+    if (j < n && wv.active(t0 + j)) wv.qk(kcur);
+  };
+  auto valu = [&](int j) {
+    if (j >= 0 && j < n && wv.active(t0 + j)) wv.softmax(p, t0 + j);
+  };
+  // copies that start in phase 2j: K(j + 1) and V(j)
+  auto copies = [&](int j, unsigned char *kdst, unsigned char *vdst) {
+    if (j + 1 < n) cp.template tile<true>(p, t0 + j + 1, kdst);
+    if (j < n) cp.template tile<false>(p, t0 + j, vdst);
+  };
+
+  if (n > 0) {
+    cp.template tile<true>(p, t0, k0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // phases 0 .. 2n+1, four at a time so that every buffer reference is static:
+    // tiles with even j use k0/v0, odd j use k1/v1
+    for (int u = 0; 4 * u <= 2 * n + 1; ++u) {
+      const int j = 2 * u;
+      copies(j, k1, v0);  // phase 4u = 2j
+      if (group_a) mfma(j, v1, k0); else valu(j - 1);
+      phase_barrier();
+      if (group_a) valu(j); else mfma(j, v1, k0);  // phase 2j + 1
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      copies(j + 1, k0, v1);  // phase 2j + 2
+      if (group_a) mfma(j + 1, v0, k1); else valu(j);
+      phase_barrier();
+      if (group_a) valu(j + 1); else mfma(j + 1, v0, k1);  // phase 2j + 3
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  }
+  wv.finish(p, wk.b, head);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -467,7 +694,11 @@ typedef void (*KernelFn)(Params);
 
 template <bool BF16, int D, int NW>
 KernelFn pick_mode(int mode) {
-  return mode ? fa_fwd_kernel<BF16, D, NW, 1> : fa_fwd_kernel<BF16, D, NW, 0>;
+  if constexpr (NW == 8) {
+    return mode ? fa_fwd_pingpong<BF16, D, 1> : fa_fwd_pingpong<BF16, D, 0>;
+  } else {
+    return mode ? fa_fwd_kernel<BF16, D, NW, 1> : fa_fwd_kernel<BF16, D, NW, 0>;
+  }
 }
 
 template <bool BF16, int D>
@@ -475,6 +706,7 @@ KernelFn pick_nw(int nw, int mode) {
   switch (nw) {
     case 1: return pick_mode<BF16, D, 1>(mode);
     case 2: return pick_mode<BF16, D, 2>(mode);
+    case 8: return pick_mode<BF16, D, 8>(mode);
     default: return pick_mode<BF16, D, 4>(mode);
   }
 }
@@ -542,7 +774,7 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
     heads_pb = tiling->heads_per_block;
     const int64_t waves32 = (int64_t)rows_pb * heads_pb;
     if (rows_pb <= 0 || heads_pb <= 0 || rows_pb % 32 != 0 || group % heads_pb != 0 ||
-        (waves32 != 32 && waves32 != 64 && waves32 != 128))
+        (waves32 != 32 && waves32 != 64 && waves32 != 128 && waves32 != 256))
       return FA_EINVAL;
   }
   if (rows_total == 0) return FA_OK;
@@ -560,6 +792,10 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   }
   if (!aligned(lse, 4) || !aligned(sinks, 4) || !aligned(mask, 4)) return FA_EUNSUPPORTED;
 
+  // the tile copies address one (b, KV head) slice of K and of V with 32-bit offsets
+  if (Tk > 0 && (64 * s.k[2] * es >= INT32_MAX || 64 * s.v[2] * es >= INT32_MAX ||
+                 ((Tk - 1) * s.k[2] + d) * es >= INT32_MAX || ((Tk - 1) * s.v[2] + d) * es >= INT32_MAX))
+    return FA_EUNSUPPORTED;
   if (rows_pb == 0) auto_tiling(B, Hkv, group, Tq, &rows_pb, &heads_pb);
   const int nw = (int)((int64_t)rows_pb * heads_pb / 32);
   const int64_t n_row_tiles = (Tq + rows_pb - 1) / rows_pb;

@@ -89,8 +89,8 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
 /*
  * Launch geometry.  A workgroup covers `rows_per_block` consecutive query rows of
  * `heads_per_block` query heads that share one KV head, so each K/V tile staged on chip
- * serves all of them.  rows_per_block * heads_per_block must be 32, 64 or 128 (one wave per
- * 32 rows of one head); heads_per_block must divide Hq / Hkv.  0 in both fields picks
+ * serves all of them.  rows_per_block * heads_per_block must be 32, 64, 128 or 256 (one wave
+ * per 32 rows of one head); heads_per_block must divide Hq / Hkv.  0 in both fields picks
  * automatically (what fa_fwd does).
  */
 typedef struct {

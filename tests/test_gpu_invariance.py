@@ -15,7 +15,7 @@ from gpu_common import bits, dev, make_inputs, say
 pytestmark = pytest.mark.gpu
 
 DTYPES = ["f32", "bf16"]
-TILINGS_G4 = [(32, 1), (64, 1), (128, 1), (32, 2), (64, 2), (32, 4)]
+TILINGS_G4 = [(32, 1), (64, 1), (128, 1), (32, 2), (64, 2), (32, 4), (64, 4), (128, 2), (256, 1)]
 
 
 def _same(a, b, what):

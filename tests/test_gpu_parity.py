@@ -102,7 +102,7 @@ def test_sentinel_every_output_written(dtype):
     B, Hq, Hkv, Tq, Tk, d = 3, 8, 2, 333, 333, 128
     q, k, v, _ = make_inputs(f"sentinel/{dtype}", B, Hq, Hkv, Tq, Tk, d, dtype)
     tq = dev(q)
-    for tiling in (None, (32, 4), (64, 2), (128, 1), (32, 1)):
+    for tiling in (None, (32, 4), (64, 2), (128, 1), (32, 1), (64, 4), (256, 1)):
         o = torch.full_like(tq, float("nan"))
         lse = torch.full((B, Hq, Tq), float("nan"), device="cuda")
         say("sentinel", dtype, tiling)
