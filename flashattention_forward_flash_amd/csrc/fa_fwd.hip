@@ -110,6 +110,23 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
+// Buffer loads that write LDS.  The resource and the builtins exist in the device pass only;
+// the host pass (which never runs kernel bodies) sees stand-ins.
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+__device__ __forceinline__ BufRsrc make_rsrc(const unsigned char *base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes < INT32_MAX ? bytes : INT32_MAX);
+  return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)n, 0x00020000 /* raw dwords */);
+}
+__device__ __forceinline__ void buf_load_lds16(BufRsrc rs, unsigned char *lds_block, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds_block, 16, off, 0, 0, 0);
+}
+#else
+typedef int BufRsrc;
+__device__ inline BufRsrc make_rsrc(const unsigned char *, int64_t) { return 0; }
+__device__ inline void buf_load_lds16(BufRsrc, unsigned char *, uint32_t) {}
+#endif
+
 
 // ds_read_b64_tr_b16 at LDS byte address `addr`.  Within each group of 16 lanes, lane r
 // supplies 4 consecutive 16-bit elements; lane i receives element i % 4 of the chunks of lanes
@@ -273,17 +290,26 @@ struct Wave {
 
   __device__ __forceinline__ bool active(int t) const { return t >= w_begin && t < w_end; }
 
-  // S^T = K Q^T for the two 32-key blocks of the tile in `kl`.  The two blocks' MFMA chains
-  // are interleaved so that consecutive MFMAs are independent.
-  __device__ __forceinline__ void qk(const unsigned char *kl) {
+  // S^T = K Q^T for the two 32-key blocks of the tile in `kl`, into `dst`.  The two blocks'
+  // MFMA chains are interleaved so that consecutive MFMAs are independent.  PIPE: the K
+  // operand reads are issued one step ahead by hand (bf16); otherwise they are left to the
+  // compiler, which can then interleave them with other work of the same block.
+  template <bool PIPE>
+  __device__ __forceinline__ void qk(const unsigned char *kl, f32x16 (&dst)[2]) const {
+    qk<PIPE>(kl, dst, [](int) {});
+  }
+  // `hook(ds)` runs after the operand reads of step ds + 1 are issued (bf16 with PIPE; before
+  // the MFMAs otherwise): the caller places the next tile's copies there, spread over the
+  // steps, so that the wave never stalls on a full memory-issue queue.
+  template <bool PIPE, typename Hook>
+  __device__ __forceinline__ void qk(const unsigned char *kl, f32x16 (&dst)[2], Hook &&hook) const {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-    if constexpr (BF16) {
+      for (int r = 0; r < 16; ++r) dst[kb][r] = 0.f;
+    if constexpr (BF16 && PIPE) {
       // K operand of step ds for both key blocks: row kb * 32 + lq, chunk (2 ds + half) swizzled
-      // by the row (key % chunks-per-row is lq % chunks-per-row for both blocks).  The reads
-      // for step ds + 1 are in flight while the MFMAs of step ds run.
+      // by the row (key % chunks-per-row is lq % chunks-per-row for both blocks).
       constexpr int NDS = D / 16;
       const uint32_t krow = lds_addr(kl) + lq * (D * 2);
       const int m = L::ksw(lq);
@@ -298,16 +324,32 @@ struct Wave {
       for (int ds = 0; ds < NDS; ++ds) {
         if (ds + 1 < NDS) {
           issue(ds + 1);
+          hook(ds);
           lds_wait<2>(ka[ds & 1][0], ka[ds & 1][1]);
         } else {
+          hook(ds);
           lds_wait<0>(ka[ds & 1][0], ka[ds & 1][1]);
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[ds & 1][kb]),
-                                                             qb[ds], sacc[kb], 0, 0, 0);
+          dst[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[ds & 1][kb]),
+                                                            qb[ds], dst[kb], 0, 0, 0);
       }
+    } else if constexpr (BF16) {
+#pragma unroll
+      for (int ds = 0; ds < D / 16; ++ds) hook(ds);
+      const unsigned char *krow = kl + lq * (D * 2);
+      const int m = L::ksw(lq);
+#pragma unroll
+      for (int ds = 0; ds < D / 16; ++ds)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(krow + kb * 32 * (D * 2) + (((2 * ds + half) ^ m) * 16));
+          dst[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ds], dst[kb], 0, 0, 0);
+        }
     } else {
+#pragma unroll
+      for (int ds = 0; ds < D / 16; ++ds) hook(ds);
 #pragma unroll
       for (int c = 0; c < D / 8; ++c) {
         f32x4 a4[2];
@@ -321,19 +363,21 @@ struct Wave {
         for (int e = 0; e < 4; ++e)
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[kb][e], qf[4 * c + e], sacc[kb], 0, 0, 0);
+            dst[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[kb][e], qf[4 * c + e], dst[kb], 0, 0, 0);
       }
     }
   }
 
-  // Online-softmax step for tile t: scores -> weights, running maximum and denominator, and
-  // the rescale of O^T.
-  __device__ __forceinline__ void softmax(const Params &p, int t) {
-    // MODE 0 (no mask, scale > 0): the row maximum is taken on the raw dot products (scaling
-    //   by a positive constant commutes with max and with fp32 rounding), and each weight is
-    //   exp2(fma(s, scale log2 e, -m)).
-    // MODE 1 (additive mask, or scale <= 0): x = fma(s, scale log2 e, mask log2 e) first.
-    const bool full = (int64_t)t * kBc >= full_lo && (int64_t)t * kBc + kBc <= full_hi;
+  __device__ __forceinline__ bool full(int t) const {
+    return (int64_t)t * kBc >= full_lo && (int64_t)t * kBc + kBc <= full_hi;
+  }
+
+  // Scores of tile t in base-2 units where needed.
+  // MODE 0 (no mask, scale > 0): the scores stay raw dot products; the row maximum is taken on
+  //   them (scaling by a positive constant commutes with max and with fp32 rounding) and each
+  //   weight is exp2(fma(s, scale log2 e, -m)).
+  // MODE 1 (additive mask, or scale <= 0): x = fma(s, scale log2 e, mask log2 e).
+  __device__ __forceinline__ void scores(const Params &p, int t, f32x16 (&sc)[2]) const {
     if constexpr (MODE == 1) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -341,25 +385,30 @@ struct Wave {
         for (int i = 0; i < 16; ++i) {
           const int key = t * kBc + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
           const float mv = (mrow && row_ok && key < p.Tk) ? mrow[(int64_t)key * p.sm_j] : 0.f;
-          sacc[kb][i] = __builtin_fmaf(sacc[kb][i], p.scale_log2, mv * kLog2e);
+          sc[kb][i] = __builtin_fmaf(sc[kb][i], p.scale_log2, mv * kLog2e);
         }
     }
-    if (!full) {  // keys this row cannot see become -inf by select
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = t * kBc + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          sacc[kb][i] = (key >= r_lo && key < r_hi) ? sacc[kb][i] : -INFINITY;
-        }
-    }
-
-    // row maximum (exact, so the reduction order is immaterial)
-    float mx = sacc[0][0];
+  }
+  // Keys this row cannot see become -inf by select (a no-op on tiles that are `full`).
+  __device__ __forceinline__ void select(int t, f32x16 (&sc)[2]) const {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+      for (int i = 0; i < 16; ++i) {
+        const int key = t * kBc + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+        sc[kb][i] = (key >= r_lo && key < r_hi) ? sc[kb][i] : -INFINITY;
+      }
+  }
+
+  // Online-softmax step on the tile's scores: running maximum and denominator, and the weights
+  // (the B operand of the PV MFMAs).  Returns alpha, the factor O^T must be multiplied by.
+  __device__ __forceinline__ float weights(const Params &p, const f32x16 (&sc)[2]) {
+    // row maximum (exact, so the reduction order is immaterial)
+    float mx = sc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     if constexpr (MODE == 0) mx = mx * p.scale_log2;  // -inf stays -inf (scale > 0)
     // The reference point m moves only when this tile's maximum exceeds it by more than
@@ -377,9 +426,9 @@ struct Wave {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if constexpr (MODE == 0)
-          w[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], p.scale_log2, -shift));
+          w[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i], p.scale_log2, -shift));
         else
-          w[kb][i] = __builtin_amdgcn_exp2f(sacc[kb][i] - shift);
+          w[kb][i] = __builtin_amdgcn_exp2f(sc[kb][i] - shift);
       }
     float s8[8];
 #pragma unroll
@@ -403,14 +452,24 @@ struct Wave {
 #pragma unroll
         for (int i = 0; i < 16; ++i) pw[kb][i] = w[kb][i];
     }
+    return alpha;
+  }
 
-    // rescale O^T (skipped when alpha == 1 in every lane: multiplying by 1 is exact)
+  // O^T *= alpha (skipped when alpha == 1 in every lane: multiplying by 1 is exact)
+  __device__ __forceinline__ void rescale(float alpha) {
     if (__ballot(alpha != 1.f)) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
+  }
+
+  // The whole online-softmax step of tile t on `sacc`.
+  __device__ __forceinline__ void softmax(const Params &p, int t) {
+    scores(p, t, sacc);
+    if (!full(t)) select(t, sacc);
+    rescale(weights(p, sacc));
   }
 
   // O^T += V^T P^T with the tile's V in `vl`.  The MFMAs are ordered key block outer, d block
@@ -548,140 +607,87 @@ struct Copier {
       voff[i] = (uint32_t)(r * p.sv_t * ES) + ((cp_chunk ^ L::vsw(r)) * 16);
     }
   }
+  // Buffer resource of tile t of K (IS_K) or V: the tile and the rest of the slice.
+  template <bool IS_K>
+  __device__ __forceinline__ BufRsrc rsrc(const Params &p, int t) const {
+    const int64_t skip = (int64_t)t * kBc * (IS_K ? p.sk_t : p.sv_t) * ES;
+    return make_rsrc((IS_K ? kbase : vbase) + skip, (IS_K ? kbytes : vbytes) - skip);
+  }
+  // Copy i of this wave's 2 * BPW copies of a tile: K blocks first, then V blocks.
+  __device__ __forceinline__ void copy(BufRsrc krs, BufRsrc vrs, int i, unsigned char *kdst,
+                                       unsigned char *vdst) const {
+    if (i < BPW) buf_load_lds16(krs, kdst + (wid * BPW + i) * 1024, koff[i]);
+    else buf_load_lds16(vrs, vdst + (wid * BPW + i - BPW) * 1024, voff[i - BPW]);
+  }
   template <bool IS_K>
   __device__ __forceinline__ void tile(const Params &p, int t, unsigned char *dst) const {
-#if defined(__HIP_DEVICE_COMPILE__)  // the buffer builtins exist in the device pass only
-    const int64_t skip = (int64_t)t * kBc * (IS_K ? p.sk_t : p.sv_t) * ES;
-    const int64_t left = (IS_K ? kbytes : vbytes) - skip;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)((IS_K ? kbase : vbase) + skip), (short)0, (int)(left < INT32_MAX ? left : INT32_MAX),
-        0x00020000 /* raw dwords */);
+    const BufRsrc rs = rsrc<IS_K>(p, t);
 #pragma unroll
-    for (int i = 0; i < BPW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void *)(dst + (wid * BPW + i) * 1024), 16,
-          IS_K ? koff[i] : voff[i], 0, 0, 0);
-#endif
+    for (int i = 0; i < BPW; ++i) buf_load_lds16(rs, dst + (wid * BPW + i) * 1024, IS_K ? koff[i] : voff[i]);
   }
 };
 
-// A workgroup-wide barrier that publishes nothing: emitted as a bare s_barrier (the memory
-// clobber keeps the compiler from moving memory accesses across it).
-__device__ __forceinline__ void phase_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
 // ---------------------------------------------------------------------------------------
-// Streaming kernel (1, 2 or 4 waves): each wave walks the tiles; the next tile is copied
-// into the other LDS buffer while the current one is used.
+// Streaming kernel (1, 2, 4 or 8 waves): each wave walks the tiles; the next tile is copied into
+// the other pair of LDS buffers while the current one is used, its copies spread over the QK
+// steps of the current tile.
 // ---------------------------------------------------------------------------------------
+// bf16 kernels are built for 2 waves per SIMD; fp32 ones (matrix-bound, larger tiles) for 1,
+// except 8-wave workgroups, which put 2 waves on each SIMD by construction.
 template <bool BF16, int D, int NW, int MODE>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 1)))
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((BF16 || NW == 8) ? 2 : 1)))
 fa_fwd_kernel(Params p) {
   using L = Layout<BF16, D>;
-  // Two LDS buffers as two objects (each [K | V]), so that the compiler can tell the copy into
-  // one from the reads of the other and does not wait for the copy before those reads.
-  __shared__ __attribute__((aligned(1024))) unsigned char smem0[2 * L::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char smem1[2 * L::TILE_BYTES];
-
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const Work wk(p);
-  const int G = p.heads_per_block;
-  const int head = wk.head_base + wid % G;
-  Wave<BF16, D, MODE> wv;
-  wv.init(p, wk.b, head, wk.row0_blk + (wid / G) * kRowsWave, lane);
-  Copier<BF16, D, NW> cp;
-  cp.init(p, wk.b, wk.kvh, wid, lane);
-
-  auto step = [&](int t, const unsigned char *kl, unsigned char *kn) {
-    if (t + 1 < wk.t_end) {  // that buffer was released by the last barrier
-      cp.template tile<true>(p, t + 1, kn);
-      cp.template tile<false>(p, t + 1, kn + L::TILE_BYTES);
-    }
-    if (wv.active(t)) {
-      wv.qk(kl);
-      wv.softmax(p, t);
-      wv.pv(kl + L::TILE_BYTES);
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile t + 1 have landed
-    __syncthreads();                // ... everyone's have, and buffer `kl` is free again
-  };
-  if (wk.t_begin < wk.t_end) {
-    cp.template tile<true>(p, wk.t_begin, smem0);
-    cp.template tile<false>(p, wk.t_begin, smem0 + L::TILE_BYTES);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-  for (int t = wk.t_begin; t < wk.t_end; t += 2) {
-    step(t, smem0, smem1);
-    if (t + 1 < wk.t_end) step(t + 1, smem1, smem0);
-  }
-  wv.finish(p, wk.b, head);
-}
-
-// ---------------------------------------------------------------------------------------
-// Ping-pong kernel (8 waves, bf16): waves 0-3 (group A) and 4-7 (group B) sit on the same
-// four SIMDs.  Time is cut into phases separated by workgroup barriers; in each phase one
-// group runs its MFMA work (PV of tile j-1, then QK of tile j) while the other runs its VALU
-// work (the softmax of a tile), and the roles swap every phase, so each SIMD always has one
-// wave feeding the matrix cores and one on the vector ALUs.  Group B runs one phase behind
-// group A.  K runs one tile ahead of V: in phase 2j the copies of K(j+1) and V(j) start
-// (into the buffers last read in phase 2j-1), and they are waited for at the end of phase
-// 2j+1.  Each row's arithmetic is exactly that of the streaming kernel.
-// ---------------------------------------------------------------------------------------
-template <bool BF16, int D, int MODE>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
-fa_fwd_pingpong(Params p) {
-  using L = Layout<BF16, D>;
+  using CP = Copier<BF16, D, NW>;
+  constexpr int NDS = D / 16;        // QK steps of a tile
+  constexpr int NCP = 2 * CP::BPW;   // copies of a tile per wave
+  // four LDS buffers as four objects, so that the compiler can tell the copies into one from
+  // the reads of another and does not wait for the copies before those reads
   __shared__ __attribute__((aligned(1024))) unsigned char k0[L::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char k1[L::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char v0[L::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char v1[L::TILE_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const bool group_a = wid < 4;
   const Work wk(p);
   const int G = p.heads_per_block;
   const int head = wk.head_base + wid % G;
   Wave<BF16, D, MODE> wv;
   wv.init(p, wk.b, head, wk.row0_blk + (wid / G) * kRowsWave, lane);
-  Copier<BF16, D, 8> cp;
+  CP cp;
   cp.init(p, wk.b, wk.kvh, wid, lane);
 
-  const int t0 = wk.t_begin, n = wk.t_end - wk.t_begin;
-  // MFMA phase of tile j: PV(j - 1) with V of tile j - 1, QK(j) with K of tile j.
-  auto mfma = [&](int j, const unsigned char *vprev, const unsigned char *kcur) {
-    if (j >= 1 && j - 1 < n && wv.active(t0 + j - 1)) wv.pv(vprev);
-    if (j < n && wv.active(t0 + j)) wv.qk(kcur);
+  auto step = [&](int t, const unsigned char *kc, const unsigned char *vc, unsigned char *kn,
+                  unsigned char *vn) {
+    const bool has_next = t + 1 < wk.t_end;  // the buffers kn, vn were released by the last barrier
+    const BufRsrc krs = cp.template rsrc<true>(p, t + 1), vrs = cp.template rsrc<false>(p, t + 1);
+    auto copies = [&](int ds) {  // copy i goes with QK step i * NDS / NCP
+      if (has_next) {
+#pragma unroll
+        for (int i = 0; i < NCP; ++i)
+          if (i * NDS / NCP == ds) cp.copy(krs, vrs, i, kn, vn);
+      }
+    };
+    if (wv.active(t)) {
+      wv.template qk<true>(kc, wv.sacc, copies);
+      wv.softmax(p, t);
+      wv.pv(vc);
+    } else {
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) copies(ds);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile t + 1 have landed
+    __syncthreads();                // ... everyone's have, and buffers kc, vc are free again
   };
-  auto valu = [&](int j) {
-    if (j >= 0 && j < n && wv.active(t0 + j)) wv.softmax(p, t0 + j);
-  };
-  // copies that start in phase 2j: K(j + 1) and V(j)
-  auto copies = [&](int j, unsigned char *kdst, unsigned char *vdst) {
-    if (j + 1 < n) cp.template tile<true>(p, t0 + j + 1, kdst);
-    if (j < n) cp.template tile<false>(p, t0 + j, vdst);
-  };
-
-  if (n > 0) {
-    cp.template tile<true>(p, t0, k0);
+  if (wk.t_begin < wk.t_end) {
+    cp.template tile<true>(p, wk.t_begin, k0);
+    cp.template tile<false>(p, wk.t_begin, v0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // phases 0 .. 2n+1, four at a time so that every buffer reference is static:
-    // tiles with even j use k0/v0, odd j use k1/v1
-    for (int u = 0; 4 * u <= 2 * n + 1; ++u) {
-      const int j = 2 * u;
-      copies(j, k1, v0);  // phase 4u = 2j
-      if (group_a) mfma(j, v1, k0); else valu(j - 1);
-      phase_barrier();
-      if (group_a) valu(j); else mfma(j, v1, k0);  // phase 2j + 1
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      copies(j + 1, k0, v1);  // phase 2j + 2
-      if (group_a) mfma(j + 1, v0, k1); else valu(j);
-      phase_barrier();
-      if (group_a) valu(j + 1); else mfma(j + 1, v0, k1);  // phase 2j + 3
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
+  }
+  for (int t = wk.t_begin; t < wk.t_end; t += 2) {
+    step(t, k0, v0, k1, v1);
+    if (t + 1 < wk.t_end) step(t + 1, k1, v1, k0, v0);
   }
   wv.finish(p, wk.b, head);
 }
@@ -694,11 +700,7 @@ typedef void (*KernelFn)(Params);
 
 template <bool BF16, int D, int NW>
 KernelFn pick_mode(int mode) {
-  if constexpr (NW == 8) {
-    return mode ? fa_fwd_pingpong<BF16, D, 1> : fa_fwd_pingpong<BF16, D, 0>;
-  } else {
-    return mode ? fa_fwd_kernel<BF16, D, NW, 1> : fa_fwd_kernel<BF16, D, NW, 0>;
-  }
+  return mode ? fa_fwd_kernel<BF16, D, NW, 1> : fa_fwd_kernel<BF16, D, NW, 0>;
 }
 
 template <bool BF16, int D>
