@@ -58,7 +58,7 @@ struct Params {
   int64_t sq_b, sq_h, sq_t, sk_b, sk_h, sk_t, sv_b, sv_h, sv_t, so_b, so_h, so_t;
   int64_t sl_b, sl_h, sm_b, sm_h, sm_i, sm_j;
   int64_t q_offset, window;
-  int32_t Tq, Tk, Hq, Hkv;
+  int32_t B, Tq, Tk, Hq, Hkv;
   int32_t group;           // Hq / Hkv
   int32_t heads_per_block; // query heads per workgroup (divides group)
   int32_t rows_per_block;  // query rows per workgroup
@@ -66,6 +66,8 @@ struct Params {
   int32_t n_row_tiles;     // ceil(Tq / rows_per_block)
   int32_t n_blocks;
   int32_t causal;
+  int32_t mask_vec;        // mask rows contiguous and 16-byte aligned: read 4 entries at a time
+  int32_t tile_major;      // order work query-tile-major (a mask shared by every (b, h))
   float scale_log2;        // scale * log2(e)
 };
 
@@ -195,10 +197,18 @@ struct Work {
     const int w = xcd_remap(blockIdx.x, p.n_blocks);
     const int hg = w % p.n_head_groups;
     int rest = w / p.n_head_groups;
-    const int rti = rest % p.n_row_tiles;
-    rest /= p.n_row_tiles;
-    kvh = rest % p.Hkv;
-    b = rest / p.Hkv;
+    int rti;
+    if (p.tile_major) {  // (row tile, b, kv head, head group): neighbours share mask rows
+      kvh = rest % p.Hkv;
+      rest /= p.Hkv;
+      b = rest % p.B;
+      rti = rest / p.B;
+    } else {             // (b, kv head, row tile, head group): neighbours share K and V
+      rti = rest % p.n_row_tiles;
+      rest /= p.n_row_tiles;
+      kvh = rest % p.Hkv;
+      b = rest / p.Hkv;
+    }
     const int rt = p.causal ? p.n_row_tiles - 1 - rti : rti;  // heavy (late) row tiles first
     head_base = kvh * p.group + hg * p.heads_per_block;
     row0_blk = rt * p.rows_per_block;
@@ -379,14 +389,31 @@ struct Wave {
   // MODE 1 (additive mask, or scale <= 0): x = fma(s, scale log2 e, mask log2 e).
   __device__ __forceinline__ void scores(const Params &p, int t, f32x16 (&sc)[2]) const {
     if constexpr (MODE == 1) {
+      float mv[2][16];
+      if (mrow && p.mask_vec && t * kBc + kBc <= p.Tk) {
+        // registers 4g..4g+3 of a block hold 4 consecutive keys: one 16-byte read
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            f32x4 m4 = {0.f, 0.f, 0.f, 0.f};
+            if (row_ok) m4 = *reinterpret_cast<const f32x4 *>(mrow + t * kBc + kb * 32 + 8 * g + 4 * half);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mv[kb][4 * g + e] = m4[e];
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = t * kBc + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+            mv[kb][i] = (mrow && row_ok && key < p.Tk) ? mrow[(int64_t)key * p.sm_j] : 0.f;
+          }
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = t * kBc + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          const float mv = (mrow && row_ok && key < p.Tk) ? mrow[(int64_t)key * p.sm_j] : 0.f;
-          sc[kb][i] = __builtin_fmaf(sc[kb][i], p.scale_log2, mv * kLog2e);
-        }
+        for (int i = 0; i < 16; ++i) sc[kb][i] = __builtin_fmaf(sc[kb][i], p.scale_log2, mv[kb][i] * kLog2e);
     }
   }
   // Keys this row cannot see become -inf by select (a no-op on tiles that are `full`).
@@ -814,6 +841,7 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   p.sm_b = s.mask[0]; p.sm_h = s.mask[1]; p.sm_i = s.mask[2]; p.sm_j = s.mask[3];
   p.q_offset = q_offset;
   p.window = window;
+  p.B = (int32_t)B;
   p.Tq = (int32_t)Tq; p.Tk = (int32_t)Tk; p.Hq = (int32_t)Hq; p.Hkv = (int32_t)Hkv;
   p.group = (int32_t)group;
   p.heads_per_block = heads_pb;
@@ -823,6 +851,9 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   p.n_blocks = (int32_t)n_blocks;
   p.causal = causal ? 1 : 0;
   p.scale_log2 = scale * kLog2e;
+  p.mask_vec = mask != nullptr && s.mask[3] == 1 && aligned(mask, 16) && s.mask[0] % 4 == 0 &&
+               s.mask[1] % 4 == 0 && s.mask[2] % 4 == 0;
+  p.tile_major = mask != nullptr && s.mask[0] == 0 && s.mask[1] == 0;
 
   const bool bf16 = dtype == FA_BF16;
   // MODE 1 when scores need the explicit form: an additive mask, or a scale that is not
