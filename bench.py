@@ -16,9 +16,11 @@ The same JSON line also reports
     headline workload.
 """
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -31,6 +33,41 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk/CU x 2.4 GHz, dense
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd TFLOP/s (causal-visible) + % MFMA peak; prefill ms @511/2044"
+
+
+KERNEL_SRC = os.path.join(ROOT, "flashattention_forward_flash_amd", "csrc", "fa_fwd.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fa_fwd_bf16_d128_causal_B8_H32_T8192_traffic.md")
+
+
+def kernel_source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline kernel from the committed counter summary, or None
+    when the summary is missing or was taken on a different kernel source."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    src = re.search(r"kernel source sha256\[:16\]: ([0-9a-f]{16})", text)
+    val = re.search(r"traffic bytes per launch: (\d+)", text)
+    if not src or not val or src.group(1) != kernel_source_hash():
+        return None
+    return int(val.group(1))
+
+
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of known size: the reference that scales the memory
+    counters (FETCH_SIZE, WRITE_SIZE) into bytes."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": reps}), flush=True)
 
 
 def visible_pairs(Tq, Tk, q_offset=0, causal=True, window=0):
@@ -200,12 +237,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--headline-only", action="store_true", help="skip the prefill / window / mask / CPU legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (reference for the memory counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (the pass shards over (b, head group) or "
               "query tiles with no exchange; multi-GPU runs are not part of it). Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
     import flashattention_forward_flash_amd as fa
     fa.load_library()
@@ -232,7 +274,9 @@ def main():
                    "global_batch": 8, "seq_len": 8192, "parallelism": "none (1 GPU)"},
         "frac_mfma_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic()},
+        "kernel_source_sha256_16": kernel_source_hash(),
         "kernel_ms": round(h["event_ms"], 4),
         "algorithmic_bytes": h["bytes"],
     }
