@@ -48,7 +48,10 @@ constexpr int kBc = 64;       // keys per tile
 constexpr int kRowsWave = 32; // query rows per wave (N of the 32x32 MFMA)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazy = 8.f;  // base-2 headroom before the running maximum is moved
+constexpr float kLazy = 8.f;
+#ifndef FA_QK_LOOKAHEAD
+#define FA_QK_LOOKAHEAD 2  // QK steps the K operand reads run ahead of the MFMAs
+#endif  // base-2 headroom before the running maximum is moved
 
 struct Params {
   const void *q, *k, *v;
@@ -323,27 +326,32 @@ struct Wave {
       constexpr int NDS = D / 16;
       const uint32_t krow = lds_addr(kl) + lq * (D * 2);
       const int m = L::ksw(lq);
-      u32x4 ka[2][2];
+      // ring of KLA + 1 steps of K operands: the reads run KLA steps ahead of the MFMAs
+      constexpr int KLA = FA_QK_LOOKAHEAD;
+      u32x4 ka[KLA + 1][2];
       auto issue = [&](int ds) {
         const uint32_t a = krow + ((((2 * ds + half) ^ m)) << 4);
-        ka[ds & 1][0] = lds_read_b128<0>(a);
-        ka[ds & 1][1] = lds_read_b128<32 * D * 2>(a);
+        ka[ds % (KLA + 1)][0] = lds_read_b128<0>(a);
+        ka[ds % (KLA + 1)][1] = lds_read_b128<32 * D * 2>(a);
       };
-      issue(0);
+#pragma unroll
+      for (int ds = 0; ds < KLA; ++ds) issue(ds);
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
-        if (ds + 1 < NDS) {
-          issue(ds + 1);
-          hook(ds);
-          lds_wait<2>(ka[ds & 1][0], ka[ds & 1][1]);
-        } else {
-          hook(ds);
-          lds_wait<0>(ka[ds & 1][0], ka[ds & 1][1]);
-        }
+        u32x4 *kc = ka[ds % (KLA + 1)];
+        if (ds + KLA < NDS) issue(ds + KLA);
+        hook(ds);
+        // reads issued after step ds's: 2 per later step already in flight
+        constexpr int dummy = 0;
+        (void)dummy;
+        const int ahead = (NDS - 1 - ds) < KLA ? (NDS - 1 - ds) : KLA;
+        if (ahead >= 3) lds_wait<6>(kc[0], kc[1]);
+        else if (ahead == 2) lds_wait<4>(kc[0], kc[1]);
+        else if (ahead == 1) lds_wait<2>(kc[0], kc[1]);
+        else lds_wait<0>(kc[0], kc[1]);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          dst[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[ds & 1][kb]),
-                                                            qb[ds], dst[kb], 0, 0, 0);
+          dst[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kc[kb]), qb[ds], dst[kb], 0, 0, 0);
       }
     } else if constexpr (BF16) {
 #pragma unroll
@@ -436,13 +444,18 @@ struct Wave {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
     if constexpr (MODE == 0) mx = mx * p.scale_log2;  // -inf stays -inf (scale > 0)
     // The reference point m moves only when this tile's maximum exceeds it by more than
     // kLazy (base-2 units), or m is still -inf: weights are then exp2(x - m) <= 2^kLazy, and
     // most tiles need no rescale.  The rule depends on the row's own scores only, so a row's
-    // bits stay independent of chunking and query tiling.
-    const float m_new = (mx > m_run + kLazy) ? mx : m_run;
+    // bits stay independent of chunking and query tiling.  The row maximum exceeds m + kLazy
+    // exactly when one lane half's maximum does, so the exchange between the halves is only
+    // needed when some lane's does.
+    float m_new = m_run;
+    if (__ballot(mx > m_run + kLazy)) {
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      m_new = (mx > m_run + kLazy) ? mx : m_run;
+    }
     const float shift = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - shift);
 
