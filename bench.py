@@ -11,7 +11,9 @@ The same JSON line also reports
   * prefill_ms: 28 back-to-back calls (one per layer, fresh seeded inputs per layer) at
     16 query / 8 KV heads, d 128: 511 tokens fp32, 2044 tokens fp32 and bf16;
   * extra workloads: the 32/8-head d 64 sliding-window (512) prefill with sinks, chunked
-    (1000, 1000, 1000, 1096) and whole, and the non-causal run with a broadcast additive mask;
+    (1000, 1000, 1000, 1096) and whole, the non-causal run with a broadcast additive mask, and
+    decode (one query row, split-KV and unsplit) at 8 x 32/8 heads x 8,192 keys bf16 and at
+    9/3 heads d 64 fp32 with 1,024 and 4,096 keys;
   * cpu_baseline: the fp64 oracle timed on the host cores over a bounded row sample of the
     headline workload.
 """
@@ -201,6 +203,35 @@ def bench_window_chunks(steps=10, warmup=3):
                 tflops=round(flops / (ev_full * 1e-3) / 1e12, 2))
 
 
+def bench_decode(steps=50, warmup=10):
+    """Decode (one query row per sequence at q_offset = Tk - 1) through split-KV (default split)
+    and through the unsplit call: the 32/8-head d 128 bf16 model at 8,192 cached keys, B = 8,
+    and the 9/3-head d 64 fp32 shape at 1,024 and 4,096 keys.  HBM-bound: rate = algorithmic
+    bytes (K, V, Q, O, LSE once) / event time of the call (both kernels for split-KV)."""
+    import torch
+    import flashattention_forward_flash_amd as fa
+    res = {}
+    for name, B, Hq, Hkv, Tk, d, dtype in (("8x32x8192_bf16_d128", 8, 32, 8, 8192, 128, "bf16"),
+                                            ("1x9x1024_f32_d64", 1, 9, 3, 1024, 64, "f32"),
+                                            ("1x9x4096_f32_d64", 1, 9, 3, 4096, 64, "f32")):
+        q, k, v = _inputs(f"decode/{name}", B, Hq, Hkv, 1, Tk, d, dtype)
+        scale = float(np.float32(1 / math.sqrt(d)))
+        out = torch.empty_like(q)
+        lse = torch.empty((B, Hq, 1), dtype=torch.float32, device="cuda")
+        split = fa.fa_splitkv_default_keys(B, Hq, Hkv, 1, Tk, Tk - 1, True, 0)
+        ws = torch.empty(fa.fa_splitkv_workspace_bytes(B, Hq, 1, Tk, d, split), dtype=torch.uint8, device="cuda")
+        print(f"[bench] decode {name} split_keys={split}", file=sys.stderr, flush=True)
+        kw = dict(scale=scale, q_offset=Tk - 1, causal=True, out=out, lse=lse)
+        _, ev_split = _timed(lambda: fa.forward_splitkv(q, k, v, split_keys=split, workspace=ws, **kw), steps, warmup)
+        _, ev_plain = _timed(lambda: fa.forward(q, k, v, **kw), steps, warmup)
+        es = q.element_size()
+        nbytes = es * (q.numel() + k.numel() + v.numel() + out.numel()) + 4 * lse.numel()
+        gbs = nbytes / (ev_split * 1e-3) / 1e9
+        res[name] = dict(split_keys=split, splitkv_us=round(ev_split * 1e3, 2), unsplit_us=round(ev_plain * 1e3, 2),
+                         algorithmic_bytes=nbytes, splitkv_GBs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+    return res
+
+
 def cpu_baseline(h, target_s=15.0):
     """The fp64 oracle on the host cores over a seeded row sample of the headline workload,
     scaled to the metric's unit (TFLOP/s over the sampled rows' visible pairs)."""
@@ -291,6 +322,7 @@ def main():
             "2044_bf16_28L": bench_prefill(2044, "bf16"),
         }
         result["window_sinks_4096"] = bench_window_chunks()
+        result["decode"] = bench_decode()
     if not args.no_cpu and not args.headline_only:
         result["cpu_baseline"] = cpu_baseline(h)
     print(json.dumps(result), flush=True)

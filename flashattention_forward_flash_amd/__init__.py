@@ -5,8 +5,10 @@ of ``csrc/fa_fwd.hip``.  PyTorch supplies device buffers and the current stream.
 no fallback: if the library is missing, importing the functions below raises.
 
 Names follow include/fa.h:
-  ``fa_fwd`` / ``fa_fwd_tiled`` / ``fa_status_str``: the C entry points over raw pointers.
-  ``forward(q, k, v, ...)``: the same call over torch tensors (strides taken from them).
+  ``fa_fwd`` / ``fa_fwd_tiled`` / ``fa_fwd_splitkv`` / ``fa_splitkv_default_keys`` /
+  ``fa_splitkv_workspace_bytes`` / ``fa_status_str``: the C entry points over raw pointers.
+  ``forward(q, k, v, ...)``, ``forward_splitkv(q, k, v, ...)``: the same calls over torch
+  tensors (strides taken from them).
 """
 import ctypes
 import math
@@ -40,7 +42,8 @@ _lib = None
 _FWD_ARGS = [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int64] * 6 + [
     ctypes.c_float, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
     ctypes.POINTER(fa_strides), ctypes.c_int, ctypes.c_void_p]
-EXPORTED = ("fa_fwd", "fa_fwd_tiled", "fa_status_str")
+EXPORTED = ("fa_fwd", "fa_fwd_splitkv", "fa_fwd_tiled", "fa_splitkv_default_keys",
+            "fa_splitkv_workspace_bytes", "fa_status_str")
 
 
 def load_library(path=None):
@@ -57,6 +60,13 @@ def load_library(path=None):
     lib.fa_fwd.argtypes = _FWD_ARGS
     lib.fa_fwd_tiled.restype = ctypes.c_int
     lib.fa_fwd_tiled.argtypes = _FWD_ARGS + [ctypes.POINTER(fa_tiling)]
+    lib.fa_fwd_splitkv.restype = ctypes.c_int
+    lib.fa_fwd_splitkv.argtypes = _FWD_ARGS + [ctypes.POINTER(fa_tiling), ctypes.c_int64, ctypes.c_void_p,
+                                               ctypes.c_size_t]
+    lib.fa_splitkv_default_keys.restype = ctypes.c_int64
+    lib.fa_splitkv_default_keys.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int, ctypes.c_int64]
+    lib.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_splitkv_workspace_bytes.argtypes = [ctypes.c_int64] * 6
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [ctypes.c_int]
     if path is None:
@@ -81,6 +91,21 @@ def fa_fwd_tiled(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, causal
                                         int(causal), window, sinks, mask, strides, dtype, stream, tiling)
 
 
+def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, causal, window, sinks, mask,
+                   strides, dtype, stream, tiling, split_keys, workspace, workspace_bytes):
+    return load_library().fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset,
+                                          int(causal), window, sinks, mask, strides, dtype, stream, tiling,
+                                          split_keys, workspace, workspace_bytes)
+
+
+def fa_splitkv_default_keys(B, Hq, Hkv, Tq, Tk, q_offset=0, causal=True, window=0):
+    return load_library().fa_splitkv_default_keys(B, Hq, Hkv, Tq, Tk, q_offset, int(causal), window)
+
+
+def fa_splitkv_workspace_bytes(B, Hq, Tq, Tk, d, split_keys):
+    return load_library().fa_splitkv_workspace_bytes(B, Hq, Tq, Tk, d, split_keys)
+
+
 def _check(status):
     if status != FA_OK:
         raise FaError(status, fa_status_str(status))
@@ -88,6 +113,32 @@ def _check(status):
 
 def forward(q, k, v, *, scale=None, q_offset=0, causal=True, window=0, sinks=None, mask=None,
             out=None, lse=None, return_lse=True, tiling=None, stream=None):
+    return _forward(q, k, v, scale, q_offset, causal, window, sinks, mask, out, lse, return_lse, tiling,
+                    stream, None, None)
+
+
+def forward_splitkv(q, k, v, *, split_keys=0, workspace=None, scale=None, q_offset=0, causal=True, window=0,
+                    sinks=None, mask=None, out=None, lse=None, return_lse=True, tiling=None, stream=None):
+    """``forward`` with the keys cut into splits of ``split_keys`` keys (a multiple of 64; 0 picks
+    ``fa_splitkv_default_keys``), the splits run in parallel and merged per row (split-KV /
+    Flash-Decoding).  ``workspace``: a GPU tensor of at least ``fa_splitkv_workspace_bytes``
+    bytes, 16-byte aligned; allocated here when None.  Results depend on ``split_keys`` (not on
+    chunking or tiling); with one split they equal ``forward``'s.
+    """
+    B, Hq, Tq, d = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    if split_keys == 0:
+        split_keys = fa_splitkv_default_keys(B, Hq, Hkv, Tq, Tk, int(q_offset), bool(causal), int(window))
+    if workspace is None:
+        import torch
+        nbytes = fa_splitkv_workspace_bytes(B, Hq, Tq, Tk, d, int(split_keys)) if split_keys > 0 else 0
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    return _forward(q, k, v, scale, q_offset, causal, window, sinks, mask, out, lse, return_lse, tiling,
+                    stream, int(split_keys), workspace)
+
+
+def _forward(q, k, v, scale, q_offset, causal, window, sinks, mask, out, lse, return_lse, tiling, stream,
+             split_keys, workspace):
     """O = softmax(scale * Q K^T + mask) V over torch tensors on the GPU.
 
     q: [B, Hq, Tq, d]; k, v: [B, Hkv, Tk, d]; float32 or bfloat16, any strides with the d axis
@@ -156,8 +207,15 @@ def forward(q, k, v, *, scale=None, q_offset=0, causal=True, window=0, sinks=Non
     til = None
     if tiling is not None:
         til = fa_tiling(int(tiling[0]), int(tiling[1]))
-    status = fa_fwd_tiled(ptr(q), ptr(k), ptr(v), ptr(out), ptr(lse), B, Hq, Hkv, Tq, Tk, d, float(scale),
-                          int(q_offset), bool(causal), int(window), ptr(sinks), mask_ptr, ctypes.byref(st),
-                          dtype, stream, ctypes.byref(til) if til is not None else None)
+    args = (ptr(q), ptr(k), ptr(v), ptr(out), ptr(lse), B, Hq, Hkv, Tq, Tk, d, float(scale), int(q_offset),
+            bool(causal), int(window), ptr(sinks), mask_ptr, ctypes.byref(st), dtype, stream,
+            ctypes.byref(til) if til is not None else None)
+    if split_keys is None:
+        status = fa_fwd_tiled(*args)
+    else:
+        if not workspace.is_cuda:
+            raise FaError(FA_EINVAL, "workspace must be a GPU tensor")
+        nbytes = workspace.numel() * workspace.element_size()
+        status = fa_fwd_splitkv(*args, split_keys, workspace.data_ptr(), nbytes)
     _check(status)
     return out, lse

@@ -20,8 +20,8 @@
 //  * The output is accumulated transposed, O^T += V^T P^T: the weights stay in the registers
 //    that computed them (the S^T accumulator layout is exactly the B-operand layout of the
 //    next MFMA once keys are permuted consistently), and the per-row rescale alpha is
-//    lane-local.  For bf16, V is stored transposed (d-major) in LDS with the key permutation
-//    applied, so each lane reads its 8 keys as one 16-byte LDS read.
+//    lane-local.  For bf16, V stays row-major in LDS and each lane gathers its V^T operand
+//    with transposing LDS reads (ds_read_b64_tr_b16).
 //  * Online softmax in base 2: x = s * scale * log2(e); p = exp2(x - m) on the hardware exp2;
 //    alpha = exp2(m_old - m_new), taken as exactly 1 when the maximum does not move and as
 //    0 when m_old = -inf (the guards of "Fused attention and softmax", exact definition
@@ -30,6 +30,7 @@
 //    source line gives the same bits on every code path (boundary or interior tile).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <type_traits>
@@ -41,6 +42,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -48,10 +50,10 @@ constexpr int kBc = 64;       // keys per tile
 constexpr int kRowsWave = 32; // query rows per wave (N of the 32x32 MFMA)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazy = 8.f;
+constexpr float kLazy = 8.f;  // base-2 headroom before the running maximum is moved
 #ifndef FA_QK_LOOKAHEAD
 #define FA_QK_LOOKAHEAD 2  // QK steps the K operand reads run ahead of the MFMAs
-#endif  // base-2 headroom before the running maximum is moved
+#endif
 
 struct Params {
   const void *q, *k, *v;
@@ -72,6 +74,14 @@ struct Params {
   int32_t mask_vec;        // mask rows contiguous and 16-byte aligned: read 4 entries at a time
   int32_t tile_major;      // order work query-tile-major (a mask shared by every (b, h))
   float scale_log2;        // scale * log2(e)
+  // Split-KV ("FlashAttention forward in C", "Going further": split-KV / Flash-Decoding).
+  // n_splits = 0: no split, rows end in o and lse.  Otherwise key split s is the absolute key
+  // range [64 s split_tiles, 64 (s + 1) split_tiles); a work item covers one split and writes
+  // its rows' online-softmax state (m, l, unnormalised acc) to the workspace, row r of split s
+  // at ws_ml[2 (s R + r)] and ws_acc[(s R + r) D] with R = B Hq Tq and r = (b Hq + h) Tq + i.
+  // The sink term belongs to split 0, the split that starts at key 0.
+  float *ws_acc, *ws_ml;
+  int32_t n_splits, split_tiles;
 };
 
 // Visible keys of absolute position pos: [vis_lo, vis_hi) ("FlashAttention forward in C",
@@ -195,20 +205,24 @@ struct Layout {
 // Work decode and the key-tile ranges of one workgroup.
 // ---------------------------------------------------------------------------------------
 struct Work {
-  int b, kvh, head_base, row0_blk, t_begin, t_end;
+  int b, kvh, head_base, row0_blk, split, t_begin, t_end;
   __device__ __forceinline__ Work(const Params &p) {
     const int w = xcd_remap(blockIdx.x, p.n_blocks);
     const int hg = w % p.n_head_groups;
     int rest = w / p.n_head_groups;
     int rti;
-    if (p.tile_major) {  // (row tile, b, kv head, head group): neighbours share mask rows
+    split = 0;
+    if (p.tile_major) {  // (row tile, split, b, kv head, head group): neighbours share mask rows
       kvh = rest % p.Hkv;
       rest /= p.Hkv;
       b = rest % p.B;
-      rti = rest / p.B;
-    } else {             // (b, kv head, row tile, head group): neighbours share K and V
+      rest /= p.B;
+      if (p.n_splits > 0) { split = rest % p.n_splits; rest /= p.n_splits; }
+      rti = rest;
+    } else {             // (b, kv head, split, row tile, head group): neighbours share K and V
       rti = rest % p.n_row_tiles;
       rest /= p.n_row_tiles;
+      if (p.n_splits > 0) { split = rest % p.n_splits; rest /= p.n_splits; }
       kvh = rest % p.Hkv;
       b = rest / p.Hkv;
     }
@@ -220,6 +234,10 @@ struct Work {
     const int last = min(row0_blk + p.rows_per_block, p.Tq) - 1;
     const int64_t lo = vis_lo(p.q_offset + row0_blk, p), hi = vis_hi(p.q_offset + last, p);
     if (hi > lo) { t_begin = (int)(lo / kBc); t_end = (int)((hi + kBc - 1) / kBc); }
+    if (p.n_splits > 0) {  // ... within this work item's key split
+      t_begin = max(t_begin, split * p.split_tiles);
+      t_end = max(t_begin, min(t_end, (split + 1) * p.split_tiles));
+    }
   }
 };
 
@@ -247,7 +265,8 @@ struct Wave {
   bf16x8 pb[BF16 ? 4 : 1];   // bf16 weights, the B operand of the PV MFMAs
   float pw[BF16 ? 1 : 2][16];  // fp32 weights (fp32 path)
 
-  __device__ __forceinline__ void init(const Params &p, int b, int head, int row0_wave, int lane_) {
+  __device__ __forceinline__ void init(const Params &p, int b, int head, int row0_wave, int lane_,
+                                       bool with_sink) {
     lane = lane_;
     half = lane >> 5;
     lq = lane & 31;
@@ -291,7 +310,7 @@ struct Wave {
     }
     m_run = -INFINITY;
     l_run = 0.f;
-    if (p.sinks) {  // a sink is the first "tile": m = z_h, l = e^0 = 1, a = 0
+    if (p.sinks && with_sink) {  // a sink is the first "tile": m = z_h, l = e^0 = 1, a = 0
       m_run = p.sinks[head] * kLog2e;
       l_run = half == 0 ? 1.f : 0.f;
     }
@@ -586,9 +605,25 @@ struct Wave {
   }
 
   // o = a / l, lse = m + ln l; a row that saw nothing gets 0 and -inf.
-  __device__ __forceinline__ void finish(const Params &p, int b, int head) {
+  __device__ __forceinline__ void finish(const Params &p, int b, int head, int split) {
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (!row_ok) return;
+    if (p.n_splits > 0) {  // split-KV: the row's state goes to the workspace as it stands
+      const int64_t r = ((int64_t)split * p.B * p.Hq + (int64_t)b * p.Hq + head) * p.Tq + row;
+      float *arow = p.ws_acc + r * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v4 = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+          *reinterpret_cast<f32x4 *>(arow + db * 32 + 8 * g + 4 * half) = v4;
+        }
+      if (half == 0) {
+        const f32x2 ml = {m_run, l_tot};
+        *reinterpret_cast<f32x2 *>(p.ws_ml + 2 * r) = ml;
+      }
+      return;
+    }
     unsigned char *orow = static_cast<unsigned char *>(p.o) +
                           ((int64_t)b * p.so_b + (int64_t)head * p.so_h + (int64_t)row * p.so_t) * ES;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -693,7 +728,7 @@ fa_fwd_kernel(Params p) {
   const int G = p.heads_per_block;
   const int head = wk.head_base + wid % G;
   Wave<BF16, D, MODE> wv;
-  wv.init(p, wk.b, head, wk.row0_blk + (wid / G) * kRowsWave, lane);
+  wv.init(p, wk.b, head, wk.row0_blk + (wid / G) * kRowsWave, lane, wk.split == 0);
   CP cp;
   cp.init(p, wk.b, wk.kvh, wid, lane);
 
@@ -729,7 +764,69 @@ fa_fwd_kernel(Params p) {
     step(t, k0, v0, k1, v1);
     if (t + 1 < wk.t_end) step(t + 1, k1, v1, k0, v0);
   }
-  wv.finish(p, wk.b, head);
+  wv.finish(p, wk.b, head, wk.split);
+}
+
+// ---------------------------------------------------------------------------------------
+// Split-KV merge ("FlashAttention forward in C", "Going further": the partial (m, l, a) of
+// the key splits are combined with the same rescale as the tiles).  One wave per query row:
+//   M = max of m_s over the splits with l_s > 0
+//   l = sum_s 2^(m_s - M) l_s,  a = sum_s 2^(m_s - M) a_s      (s ascending, fixed order)
+//   o = l > 0 ? a * (1 / l) : 0,  lse = l > 0 ? (M + log2 l) ln 2 : -inf
+// With one split this is the epilogue of the unsplit kernel, bit for bit.
+// ---------------------------------------------------------------------------------------
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void fa_merge_kernel(Params p) {
+  constexpr int EPL = D / 64;  // elements per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = (int64_t)p.B * p.Hq * p.Tq;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int i = (int)(r % p.Tq);
+  const int64_t bh = r / p.Tq;
+  const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
+
+  float M = -INFINITY;
+  for (int s = 0; s < p.n_splits; ++s) {
+    const f32x2 ml = *reinterpret_cast<const f32x2 *>(p.ws_ml + 2 * ((int64_t)s * rows + r));
+    if (ml[1] > 0.f) M = fmaxf(M, ml[0]);
+  }
+  float l = 0.f, a[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) a[e] = 0.f;
+  for (int s = 0; s < p.n_splits; ++s) {
+    const int64_t rs = (int64_t)s * rows + r;
+    const f32x2 ml = *reinterpret_cast<const f32x2 *>(p.ws_ml + 2 * rs);
+    if (!(ml[1] > 0.f)) continue;
+    const float w = __builtin_amdgcn_exp2f(ml[0] - M);
+    l = l + w * ml[1];
+    const float *as = p.ws_acc + rs * D + EPL * lane;
+    if constexpr (EPL == 2) {
+      const f32x2 v = *reinterpret_cast<const f32x2 *>(as);
+      a[0] = a[0] + w * v[0];
+      a[1] = a[1] + w * v[1];
+    } else {
+      a[0] = a[0] + w * as[0];
+    }
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  unsigned char *orow = static_cast<unsigned char *>(p.o) +
+                        ((int64_t)b * p.so_b + (int64_t)h * p.so_h + (int64_t)i * p.so_t) * (BF16 ? 2 : 4);
+  if constexpr (BF16) {
+    if constexpr (EPL == 2)
+      *reinterpret_cast<uint32_t *>(orow + 4 * lane) = pack_bf16x2(a[0] * inv, a[1] * inv);
+    else
+      *reinterpret_cast<unsigned short *>(orow + 2 * lane) = __builtin_bit_cast(unsigned short, (__bf16)(a[0] * inv));
+  } else {
+    if constexpr (EPL == 2) {
+      const f32x2 v = {a[0] * inv, a[1] * inv};
+      *reinterpret_cast<f32x2 *>(orow + 8 * lane) = v;
+    } else {
+      *reinterpret_cast<float *>(orow + 4 * lane) = a[0] * inv;
+    }
+  }
+  if (p.lse && lane == 0)
+    p.lse[(int64_t)b * p.sl_b + (int64_t)h * p.sl_h + i] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -773,11 +870,45 @@ void auto_tiling(int64_t B, int64_t Hkv, int64_t group, int64_t Tq, int32_t *row
   }
 }
 
+// Geometry of a split-KV call: the splits supply the parallelism, so a workgroup takes as many
+// heads of one KV group as divide it (up to 4, sharing each staged K/V tile) and at most 4
+// waves; a decode row (Tq = 1) then costs one wave per head.
+void split_tiling(int64_t group, int64_t Tq, int32_t *rows, int32_t *heads) {
+  const int g = group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+  int nw = g;
+  while (nw < 4 && (int64_t)32 * nw / g < Tq) nw *= 2;
+  *heads = g;
+  *rows = 32 * nw / g;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Split size (keys, a multiple of 64) for fa_fwd_splitkv when the caller has none: enough
+// splits over the keys some row can see that the work items fill a 256-CU part twice, and at
+// least 4 tiles per split.  A function of the sizes only, so results do not depend on the device.
+int64_t default_split_keys(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk,
+                           int64_t q_offset, int causal, int64_t window) {
+  if (Hkv <= 0 || Tq <= 0 || Tk <= 0 || B <= 0) return 64;
+  const int64_t group = Hq / Hkv;
+  int32_t rows = 0, heads = 0;
+  split_tiling(group, Tq, &rows, &heads);
+  const int64_t base = B * Hkv * (group / heads) * ceil_div(Tq, rows);
+  const int64_t hi = causal ? std::min(Tk, q_offset + Tq) : Tk;
+  const int64_t lo = window > 0 ? std::max((int64_t)0, q_offset - window + 1) : 0;
+  const int64_t tiles = hi > lo ? ceil_div(hi, 64) - lo / 64 : 1;
+  const int64_t want = std::max((int64_t)1, ceil_div(512, base));
+  return 64 * std::max((int64_t)4, ceil_div(tiles, want));
+}
+
+int64_t n_splits_of(int64_t Tk, int64_t split_keys) { return std::max((int64_t)1, ceil_div(Tk, split_keys)); }
+
 fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
                    int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d, float scale,
                    int64_t q_offset, int causal, int64_t window, const float *sinks,
                    const float *mask, const fa_strides *strides, fa_dtype dtype, void *stream,
-                   const fa_tiling *tiling) {
+                   const fa_tiling *tiling, int64_t split_keys = 0, void *workspace = nullptr,
+                   size_t workspace_bytes = 0) {
+  const bool split = split_keys != 0;
   // ---- arguments ----
   if (B < 0 || Hq < 0 || Hkv < 0 || Tq < 0 || Tk < 0 || q_offset < 0 || d <= 0) return FA_EINVAL;
   if (!std::isfinite(scale)) return FA_EINVAL;
@@ -819,6 +950,17 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
         (waves32 != 32 && waves32 != 64 && waves32 != 128 && waves32 != 256))
       return FA_EINVAL;
   }
+  int64_t n_splits = 0;
+  if (split) {
+    if (split_keys < 0 || split_keys % 64 != 0) return FA_EINVAL;
+    n_splits = n_splits_of(Tk, split_keys);
+    if (rows_total > 0) {
+      if (workspace == nullptr) return FA_EINVAL;
+      if (n_splits > INT32_MAX / 4 || rows_total > INT64_MAX / (4 * (d + 2)) / n_splits) return FA_EUNSUPPORTED;
+      if ((uint64_t)workspace_bytes < (uint64_t)(n_splits * rows_total * (d + 2) * 4)) return FA_EINVAL;
+      if (!aligned(workspace, 16)) return FA_EUNSUPPORTED;
+    }
+  }
   if (rows_total == 0) return FA_OK;
 
   // ---- alignment of the vector loads and stores ----
@@ -838,11 +980,14 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   if (Tk > 0 && (64 * s.k[2] * es >= INT32_MAX || 64 * s.v[2] * es >= INT32_MAX ||
                  ((Tk - 1) * s.k[2] + d) * es >= INT32_MAX || ((Tk - 1) * s.v[2] + d) * es >= INT32_MAX))
     return FA_EUNSUPPORTED;
-  if (rows_pb == 0) auto_tiling(B, Hkv, group, Tq, &rows_pb, &heads_pb);
+  if (rows_pb == 0) {
+    if (split) split_tiling(group, Tq, &rows_pb, &heads_pb);
+    else auto_tiling(B, Hkv, group, Tq, &rows_pb, &heads_pb);
+  }
   const int nw = (int)((int64_t)rows_pb * heads_pb / 32);
   const int64_t n_row_tiles = (Tq + rows_pb - 1) / rows_pb;
-  const int64_t n_blocks = B * Hkv * (group / heads_pb) * n_row_tiles;
-  if (n_blocks > INT32_MAX) return FA_EUNSUPPORTED;
+  const int64_t n_blocks = B * Hkv * (group / heads_pb) * n_row_tiles * (split ? n_splits : 1);
+  if (n_blocks > INT32_MAX || (split && rows_total / 4 + 1 > INT32_MAX)) return FA_EUNSUPPORTED;
 
   Params p;
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.sinks = sinks; p.mask = mask;
@@ -867,6 +1012,10 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   p.mask_vec = mask != nullptr && s.mask[3] == 1 && aligned(mask, 16) && s.mask[0] % 4 == 0 &&
                s.mask[1] % 4 == 0 && s.mask[2] % 4 == 0;
   p.tile_major = mask != nullptr && s.mask[0] == 0 && s.mask[1] == 0;
+  p.n_splits = (int32_t)n_splits;
+  p.split_tiles = split ? (int32_t)std::min(split_keys / 64, (int64_t)INT32_MAX / 4) : 0;
+  p.ws_acc = split ? static_cast<float *>(workspace) : nullptr;
+  p.ws_ml = split ? static_cast<float *>(workspace) + n_splits * rows_total * d : nullptr;
 
   const bool bf16 = dtype == FA_BF16;
   // MODE 1 when scores need the explicit form: an additive mask, or a scale that is not
@@ -877,7 +1026,15 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   (void)hipGetLastError();  // clear a stale error so the check below reports this launch
   hipLaunchKernelGGL(fn, dim3((unsigned)n_blocks), dim3(nw * 64), 0,
                      static_cast<hipStream_t>(stream), p);
-  return hipGetLastError() == hipSuccess ? FA_OK : FA_EDEVICE;
+  if (hipGetLastError() != hipSuccess) return FA_EDEVICE;
+  if (split) {  // merge the splits' row states into o and lse (same stream, so after the above)
+    void (*merge)(Params) = bf16 ? (d == 64 ? fa_merge_kernel<true, 64> : fa_merge_kernel<true, 128>)
+                                 : (d == 64 ? fa_merge_kernel<false, 64> : fa_merge_kernel<false, 128>);
+    hipLaunchKernelGGL(merge, dim3((unsigned)((rows_total + 3) / 4)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), p);
+    if (hipGetLastError() != hipSuccess) return FA_EDEVICE;
+  }
+  return FA_OK;
 }
 
 }  // namespace
@@ -899,6 +1056,32 @@ fa_status fa_fwd_tiled(const void *q, const void *k, const void *v, void *o, flo
                        fa_dtype dtype, void *stream, const fa_tiling *tiling) {
   return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, causal, window, sinks,
                   mask, strides, dtype, stream, tiling);
+}
+
+fa_status fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                          int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                          float scale, int64_t q_offset, int causal, int64_t window,
+                          const float *sinks, const float *mask, const fa_strides *strides,
+                          fa_dtype dtype, void *stream, const fa_tiling *tiling, int64_t split_keys,
+                          void *workspace, size_t workspace_bytes) {
+  if (split_keys == 0) split_keys = fa_splitkv_default_keys(B, Hq, Hkv, Tq, Tk, q_offset, causal, window);
+  if (split_keys <= 0) return FA_EINVAL;
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, causal, window, sinks,
+                  mask, strides, dtype, stream, tiling, split_keys, workspace, workspace_bytes);
+}
+
+int64_t fa_splitkv_default_keys(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk,
+                                int64_t q_offset, int causal, int64_t window) {
+  return default_split_keys(B, Hq, Hkv, Tq, Tk, q_offset, causal, window);
+}
+
+size_t fa_splitkv_workspace_bytes(int64_t B, int64_t Hq, int64_t Tq, int64_t Tk, int64_t d,
+                                  int64_t split_keys) {
+  if (B < 0 || Hq < 0 || Tq < 0 || Tk < 0 || d <= 0 || split_keys <= 0) return 0;
+  const int64_t rows = B * Hq * Tq;
+  const int64_t ns = n_splits_of(Tk, split_keys);
+  if (rows > 0 && (ns > INT64_MAX / (4 * (d + 2)) / rows)) return 0;
+  return (size_t)(ns * rows * (d + 2) * 4);
 }
 
 const char *fa_status_str(fa_status s) {

@@ -25,6 +25,7 @@
 #ifndef FA_H
 #define FA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -109,6 +110,56 @@ fa_status fa_fwd_tiled(const void *q, const void *k, const void *v, void *o, flo
                        float scale, int64_t q_offset, int causal, int64_t window,
                        const float *sinks, const float *mask, const fa_strides *strides,
                        fa_dtype dtype, void *stream, const fa_tiling *tiling);
+
+/*
+ * Split-KV ("FlashAttention forward in C", "Going further": split-KV / Flash-Decoding).  For
+ * calls with few query rows and many keys (decoding: Tq = 1, q_offset = Tk - 1), where one
+ * workgroup per query tile leaves most of the GPU idle, the keys are cut into splits of
+ * `split_keys` keys at absolute positions [s * split_keys, (s + 1) * split_keys).  One kernel
+ * runs every (query tile, split) pair and keeps each row's online-softmax state (m, l, a) of
+ * its split; a second kernel merges the splits of each row with the tile rescale, in
+ * ascending split order:
+ *
+ *   M = max_s m_s,  l = sum_s e^{m_s - M} l_s,  a = sum_s e^{m_s - M} a_s,  o = a / l,
+ *   lse = M + ln l                      (splits with l_s = 0 are left out; the sink term
+ *                                        belongs to split 0)
+ *
+ * which is the same o and lse as fa_fwd up to rounding (the pages: trading invariance for
+ * parallelism).  The bits of a row depend on q_i, K, V, p_i, the flags, d, the dtype and
+ * split_keys only: not on chunking, tiling, batch, strides or launch order.  With a single
+ * split (split_keys >= Tk) the results equal fa_fwd's bit for bit (the sign of a zero aside).
+ *
+ * Arguments as for fa_fwd_tiled, plus:
+ *   split_keys       keys per split, a positive multiple of 64; 0 picks
+ *                    fa_splitkv_default_keys(...).  Anything else returns FA_EINVAL.
+ *   workspace        device memory owned by the caller, 16-byte aligned, at least
+ *                    fa_splitkv_workspace_bytes(B, Hq, Tq, Tk, d, split_keys) bytes (else
+ *                    FA_EINVAL; misaligned: FA_EUNSUPPORTED).  Its contents on entry do not
+ *                    matter; it holds the per-split row states afterwards.  Calls that
+ *                    overlap in time need workspaces of their own.
+ * Both kernels are enqueued on `stream`; the library allocates nothing.
+ */
+fa_status fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                         float scale, int64_t q_offset, int causal, int64_t window,
+                         const float *sinks, const float *mask, const fa_strides *strides,
+                         fa_dtype dtype, void *stream, const fa_tiling *tiling, int64_t split_keys,
+                         void *workspace, size_t workspace_bytes);
+
+/*
+ * The split size fa_fwd_splitkv takes for split_keys = 0: a multiple of 64 (at least 256)
+ * that cuts the keys some row can see into enough splits to give a 256-CU device about 512
+ * workgroups.  It depends on the arguments only, not on the device.
+ */
+int64_t fa_splitkv_default_keys(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk,
+                                int64_t q_offset, int causal, int64_t window);
+
+/*
+ * Workspace bytes fa_fwd_splitkv needs: (d + 2) * 4 bytes per (split, row), with
+ * max(1, ceil(Tk / split_keys)) splits and B * Hq * Tq rows.  0 for invalid arguments.
+ */
+size_t fa_splitkv_workspace_bytes(int64_t B, int64_t Hq, int64_t Tq, int64_t Tk, int64_t d,
+                                  int64_t split_keys);
 
 /* Static English name of a status code (never NULL). */
 const char *fa_status_str(fa_status s);

@@ -98,3 +98,49 @@ def test_empty_work_returns_ok_without_launch():
     assert _call(B=0) == fa.FA_OK
     assert _call(Hq=0, Hkv=0, q=None, o=None) == fa.FA_OK
     assert _call(Tq=0, q=None, o=None, k=None, v=None) == fa.FA_OK
+
+
+def _split_call(split_keys=256, ws=P, ws_bytes=1 << 30, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Hq=4, Hkv=2, Tq=1, Tk=1000, d=64, scale=0.125, q_offset=999,
+             causal=1, window=0, sinks=None, mask=None, strides=None, dtype=fa.FA_F32, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Tq"],
+                             a["Tk"], a["d"], a["scale"], a["q_offset"], a["causal"], a["window"], a["sinks"],
+                             a["mask"], a["strides"], a["dtype"], a["stream"], None, split_keys, ws, ws_bytes)
+
+
+def test_splitkv_workspace_bytes():
+    # (d + 2) * 4 bytes per (split, row); splits = max(1, ceil(Tk / split_keys))
+    assert fa.fa_splitkv_workspace_bytes(2, 4, 8, 1000, 64, 256) == 4 * (2 * 4 * 8) * 66 * 4
+    assert fa.fa_splitkv_workspace_bytes(8, 32, 1, 8192, 128, 1024) == 8 * 256 * 130 * 4
+    assert fa.fa_splitkv_workspace_bytes(1, 4, 3, 0, 128, 64) == 1 * 12 * 130 * 4
+    assert fa.fa_splitkv_workspace_bytes(1, 4, 0, 100, 128, 64) == 0
+    assert fa.fa_splitkv_workspace_bytes(1, 4, 3, 100, 128, 0) == 0
+    assert fa.fa_splitkv_workspace_bytes(-1, 4, 3, 100, 128, 64) == 0
+
+
+def test_splitkv_default_keys():
+    # decode at 8 x 32/8 heads x 8192 keys: 64 work items per split -> 8 splits of 1024 keys
+    assert fa.fa_splitkv_default_keys(8, 32, 8, 1, 8192, 8191, True, 0) == 1024
+    for args in ((1, 9, 3, 1, 4096, 4095, True, 0), (1, 16, 8, 511, 511, 0, True, 0),
+                 (1, 32, 8, 1, 100000, 99999, True, 4096), (4, 4, 4, 7, 7, 0, False, 0), (1, 1, 1, 1, 0, 0, True, 0)):
+        s = fa.fa_splitkv_default_keys(*args)
+        assert s >= 64 and s % 64 == 0, (args, s)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(split_keys=100), fa.FA_EINVAL),           # not a multiple of 64
+    (dict(split_keys=-64), fa.FA_EINVAL),
+    (dict(ws=None), fa.FA_EINVAL),                  # no workspace
+    (dict(ws_bytes=1000), fa.FA_EINVAL),            # workspace too small (4 splits x 4 rows x 66 x 4)
+    (dict(ws=P + 8), fa.FA_EUNSUPPORTED),           # workspace not 16-byte aligned
+    (dict(Hq=6, Hkv=4), fa.FA_ESHAPE),
+    (dict(d=96), fa.FA_EUNSUPPORTED),
+])
+def test_splitkv_validation_errors(kw, want):
+    assert _split_call(**kw) == want
+
+
+def test_splitkv_empty_work_returns_ok_without_launch():
+    assert _split_call(Tq=0) == fa.FA_OK
+    assert _split_call(B=0, ws=None, ws_bytes=0) == fa.FA_OK
