@@ -218,7 +218,8 @@ def bench_decode(steps=50, warmup=10):
         scale = float(np.float32(1 / math.sqrt(d)))
         out = torch.empty_like(q)
         lse = torch.empty((B, Hq, 1), dtype=torch.float32, device="cuda")
-        split = fa.fa_splitkv_default_keys(B, Hq, Hkv, 1, Tk, Tk - 1, True, 0)
+        split = fa.fa_splitkv_default_keys(B, Hq, Hkv, 1, Tk, Tk - 1, True, 0,
+                                           fa.FA_BF16 if dtype == "bf16" else fa.FA_F32)
         ws = torch.empty(fa.fa_splitkv_workspace_bytes(B, Hq, 1, Tk, d, split), dtype=torch.uint8, device="cuda")
         print(f"[bench] decode {name} split_keys={split}", file=sys.stderr, flush=True)
         kw = dict(scale=scale, q_offset=Tk - 1, causal=True, out=out, lse=lse)

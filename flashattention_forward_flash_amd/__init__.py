@@ -64,7 +64,7 @@ def load_library(path=None):
     lib.fa_fwd_splitkv.argtypes = _FWD_ARGS + [ctypes.POINTER(fa_tiling), ctypes.c_int64, ctypes.c_void_p,
                                                ctypes.c_size_t]
     lib.fa_splitkv_default_keys.restype = ctypes.c_int64
-    lib.fa_splitkv_default_keys.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int, ctypes.c_int64]
+    lib.fa_splitkv_default_keys.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int, ctypes.c_int64, ctypes.c_int]
     lib.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_splitkv_workspace_bytes.argtypes = [ctypes.c_int64] * 6
     lib.fa_status_str.restype = ctypes.c_char_p
@@ -98,8 +98,8 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, caus
                                           split_keys, workspace, workspace_bytes)
 
 
-def fa_splitkv_default_keys(B, Hq, Hkv, Tq, Tk, q_offset=0, causal=True, window=0):
-    return load_library().fa_splitkv_default_keys(B, Hq, Hkv, Tq, Tk, q_offset, int(causal), window)
+def fa_splitkv_default_keys(B, Hq, Hkv, Tq, Tk, q_offset=0, causal=True, window=0, dtype=FA_BF16):
+    return load_library().fa_splitkv_default_keys(B, Hq, Hkv, Tq, Tk, q_offset, int(causal), window, dtype)
 
 
 def fa_splitkv_workspace_bytes(B, Hq, Tq, Tk, d, split_keys):
@@ -125,12 +125,13 @@ def forward_splitkv(q, k, v, *, split_keys=0, workspace=None, scale=None, q_offs
     bytes, 16-byte aligned; allocated here when None.  Results depend on ``split_keys`` (not on
     chunking or tiling); with one split they equal ``forward``'s.
     """
+    import torch
     B, Hq, Tq, d = q.shape
     Hkv, Tk = k.shape[1], k.shape[2]
     if split_keys == 0:
-        split_keys = fa_splitkv_default_keys(B, Hq, Hkv, Tq, Tk, int(q_offset), bool(causal), int(window))
+        dtype = FA_BF16 if q.dtype == torch.bfloat16 else FA_F32
+        split_keys = fa_splitkv_default_keys(B, Hq, Hkv, Tq, Tk, int(q_offset), bool(causal), int(window), dtype)
     if workspace is None:
-        import torch
         nbytes = fa_splitkv_workspace_bytes(B, Hq, Tq, Tk, d, int(split_keys)) if split_keys > 0 else 0
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     return _forward(q, k, v, scale, q_offset, causal, window, sinks, mask, out, lse, return_lse, tiling,

@@ -785,28 +785,59 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(Params p) {
   const int i = (int)(r % p.Tq);
   const int64_t bh = r / p.Tq;
   const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
+  const f32x2 *ml = reinterpret_cast<const f32x2 *>(p.ws_ml) + r;  // split s at ml[s * rows]
 
+  // M: lane s reads split s's state (64 splits at a time); the maximum is exact in any order
   float M = -INFINITY;
-  for (int s = 0; s < p.n_splits; ++s) {
-    const f32x2 ml = *reinterpret_cast<const f32x2 *>(p.ws_ml + 2 * ((int64_t)s * rows + r));
-    if (ml[1] > 0.f) M = fmaxf(M, ml[0]);
+  for (int s = lane; s < p.n_splits; s += 64) {
+    const f32x2 st = ml[(int64_t)s * rows];
+    if (st[1] > 0.f) M = fmaxf(M, st[0]);
   }
+#pragma unroll
+  for (int x = 1; x < 64; x <<= 1) M = fmaxf(M, __shfl_xor(M, x));
+
+  // l and a summed over the splits in ascending order; split s has weight w_s = 2^(m_s - M),
+  // 0 when it saw no key.  Lane s computes w_s, and every lane takes the weights in order.
   float l = 0.f, a[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) a[e] = 0.f;
-  for (int s = 0; s < p.n_splits; ++s) {
-    const int64_t rs = (int64_t)s * rows + r;
-    const f32x2 ml = *reinterpret_cast<const f32x2 *>(p.ws_ml + 2 * rs);
-    if (!(ml[1] > 0.f)) continue;
-    const float w = __builtin_amdgcn_exp2f(ml[0] - M);
-    l = l + w * ml[1];
-    const float *as = p.ws_acc + rs * D + EPL * lane;
-    if constexpr (EPL == 2) {
-      const f32x2 v = *reinterpret_cast<const f32x2 *>(as);
-      a[0] = a[0] + w * v[0];
-      a[1] = a[1] + w * v[1];
-    } else {
-      a[0] = a[0] + w * as[0];
+  for (int s0 = 0; s0 < p.n_splits; s0 += 64) {
+    float w = 0.f, ls = 0.f;
+    if (s0 + lane < p.n_splits) {
+      const f32x2 st = ml[(int64_t)(s0 + lane) * rows];
+      if (st[1] > 0.f) { w = __builtin_amdgcn_exp2f(st[0] - M); ls = st[1]; }
+    }
+    const int n = min(64, p.n_splits - s0);
+    for (int j0 = 0; j0 < n; j0 += 8) {  // 8 splits' accumulator loads in flight at a time
+      float wj[8], lj[8], v[8][EPL];
+      bool any = false;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        wj[j] = __shfl(w, (j0 + j) & 63);
+        lj[j] = __shfl(ls, (j0 + j) & 63);
+        if (j0 + j >= n) wj[j] = 0.f;
+        any |= wj[j] > 0.f;
+      }
+      if (!any) continue;  // splits that saw no key of this row add nothing
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int s = s0 + j0 + j;
+        if (j0 + j < n) {
+          const float *as = p.ws_acc + ((int64_t)s * rows + r) * D + EPL * lane;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) v[j][e] = as[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) v[j][e] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (!(wj[j] > 0.f)) continue;
+        l = l + wj[j] * lj[j];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) a[e] = a[e] + wj[j] * v[j][e];
+      }
     }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -884,10 +915,11 @@ void split_tiling(int64_t group, int64_t Tq, int32_t *rows, int32_t *heads) {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Split size (keys, a multiple of 64) for fa_fwd_splitkv when the caller has none: enough
-// splits over the keys some row can see that the work items fill a 256-CU part twice, and at
-// least 4 tiles per split.  A function of the sizes only, so results do not depend on the device.
+// splits over the keys some row can see that the work items fill a 256-CU part twice, with at
+// least 4 tiles per split for bf16 and 2 for fp32 (whose tiles cost more arithmetic).  A
+// function of the arguments only, so results do not depend on the device.
 int64_t default_split_keys(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk,
-                           int64_t q_offset, int causal, int64_t window) {
+                           int64_t q_offset, int causal, int64_t window, fa_dtype dtype) {
   if (Hkv <= 0 || Tq <= 0 || Tk <= 0 || B <= 0) return 64;
   const int64_t group = Hq / Hkv;
   int32_t rows = 0, heads = 0;
@@ -897,7 +929,7 @@ int64_t default_split_keys(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64
   const int64_t lo = window > 0 ? std::max((int64_t)0, q_offset - window + 1) : 0;
   const int64_t tiles = hi > lo ? ceil_div(hi, 64) - lo / 64 : 1;
   const int64_t want = std::max((int64_t)1, ceil_div(512, base));
-  return 64 * std::max((int64_t)4, ceil_div(tiles, want));
+  return 64 * std::max((int64_t)(dtype == FA_BF16 ? 4 : 2), ceil_div(tiles, want));
 }
 
 int64_t n_splits_of(int64_t Tk, int64_t split_keys) { return std::max((int64_t)1, ceil_div(Tk, split_keys)); }
@@ -1064,15 +1096,15 @@ fa_status fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, f
                           const float *sinks, const float *mask, const fa_strides *strides,
                           fa_dtype dtype, void *stream, const fa_tiling *tiling, int64_t split_keys,
                           void *workspace, size_t workspace_bytes) {
-  if (split_keys == 0) split_keys = fa_splitkv_default_keys(B, Hq, Hkv, Tq, Tk, q_offset, causal, window);
+  if (split_keys == 0) split_keys = fa_splitkv_default_keys(B, Hq, Hkv, Tq, Tk, q_offset, causal, window, dtype);
   if (split_keys <= 0) return FA_EINVAL;
   return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, causal, window, sinks,
                   mask, strides, dtype, stream, tiling, split_keys, workspace, workspace_bytes);
 }
 
 int64_t fa_splitkv_default_keys(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk,
-                                int64_t q_offset, int causal, int64_t window) {
-  return default_split_keys(B, Hq, Hkv, Tq, Tk, q_offset, causal, window);
+                                int64_t q_offset, int causal, int64_t window, fa_dtype dtype) {
+  return default_split_keys(B, Hq, Hkv, Tq, Tk, q_offset, causal, window, dtype);
 }
 
 size_t fa_splitkv_workspace_bytes(int64_t B, int64_t Hq, int64_t Tq, int64_t Tk, int64_t d,

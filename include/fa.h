@@ -147,12 +147,12 @@ fa_status fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, f
                          void *workspace, size_t workspace_bytes);
 
 /*
- * The split size fa_fwd_splitkv takes for split_keys = 0: a multiple of 64 (at least 256)
- * that cuts the keys some row can see into enough splits to give a 256-CU device about 512
- * workgroups.  It depends on the arguments only, not on the device.
+ * The split size fa_fwd_splitkv takes for split_keys = 0: a multiple of 64 (at least 256 for
+ * bf16, 128 for fp32) that cuts the keys some row can see into enough splits to give a
+ * 256-CU device about 512 workgroups.  It depends on the arguments only, not on the device.
  */
 int64_t fa_splitkv_default_keys(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk,
-                                int64_t q_offset, int causal, int64_t window);
+                                int64_t q_offset, int causal, int64_t window, fa_dtype dtype);
 
 /*
  * Workspace bytes fa_fwd_splitkv needs: (d + 2) * 4 bytes per (split, row), with

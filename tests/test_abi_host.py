@@ -121,11 +121,15 @@ def test_splitkv_workspace_bytes():
 
 def test_splitkv_default_keys():
     # decode at 8 x 32/8 heads x 8192 keys: 64 work items per split -> 8 splits of 1024 keys
-    assert fa.fa_splitkv_default_keys(8, 32, 8, 1, 8192, 8191, True, 0) == 1024
+    assert fa.fa_splitkv_default_keys(8, 32, 8, 1, 8192, 8191, True, 0, fa.FA_BF16) == 1024
+    # 9 work items per split: the 64 visible tiles cut into the minimum split (4 tiles bf16, 2 fp32)
+    assert fa.fa_splitkv_default_keys(1, 9, 3, 1, 4096, 4095, True, 0, fa.FA_BF16) == 256
+    assert fa.fa_splitkv_default_keys(1, 9, 3, 1, 4096, 4095, True, 0, fa.FA_F32) == 128
     for args in ((1, 9, 3, 1, 4096, 4095, True, 0), (1, 16, 8, 511, 511, 0, True, 0),
                  (1, 32, 8, 1, 100000, 99999, True, 4096), (4, 4, 4, 7, 7, 0, False, 0), (1, 1, 1, 1, 0, 0, True, 0)):
-        s = fa.fa_splitkv_default_keys(*args)
-        assert s >= 64 and s % 64 == 0, (args, s)
+        for dt in (fa.FA_F32, fa.FA_BF16):
+            s = fa.fa_splitkv_default_keys(*args, dt)
+            assert s >= 64 and s % 64 == 0, (args, s)
 
 
 @pytest.mark.parametrize("kw,want", [

@@ -181,7 +181,7 @@ def test_decode_model_shape_bf16():
     q, k, v, _ = make_inputs("splitkv/decode8192", B, Hq, Hkv, 1, Tk, d, "bf16")
     tq, tk, tv = dev(q), dev(k), dev(v)
     kw = dict(scale=scale_for(d), q_offset=Tk - 1, causal=True)
-    say("splitkv decode 8x32x8192 bf16", fa.fa_splitkv_default_keys(B, Hq, Hkv, 1, Tk, Tk - 1, True, 0))
+    say("splitkv decode 8x32x8192 bf16", fa.fa_splitkv_default_keys(B, Hq, Hkv, 1, Tk, Tk - 1, True, 0, fa.FA_BF16))
     o, lse = fa.forward_splitkv(tq, tk, tv, **kw)
     o1, l1 = fa.forward(tq, tk, tv, **kw)
     torch.cuda.synchronize()
