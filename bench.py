@@ -203,11 +203,28 @@ def bench_window_chunks(steps=10, warmup=3):
                 tflops=round(flops / (ev_full * 1e-3) / 1e12, 2))
 
 
+def _timed_batch(fn, steps, warmup):
+    """Mean ms per call of `steps` back-to-back calls between one pair of events (for calls
+    short enough that an event pair per call would time the launch path rather than the work)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
 def bench_decode(steps=50, warmup=10):
     """Decode (one query row per sequence at q_offset = Tk - 1) through split-KV (default split)
     and through the unsplit call: the 32/8-head d 128 bf16 model at 8,192 cached keys, B = 8,
     and the 9/3-head d 64 fp32 shape at 1,024 and 4,096 keys.  HBM-bound: rate = algorithmic
-    bytes (K, V, Q, O, LSE once) / event time of the call (both kernels for split-KV)."""
+    bytes (K, V, Q, O, LSE once) / time per call (both kernels for split-KV), calls back to
+    back between one pair of events."""
     import torch
     import flashattention_forward_flash_amd as fa
     res = {}
@@ -223,13 +240,26 @@ def bench_decode(steps=50, warmup=10):
         ws = torch.empty(fa.fa_splitkv_workspace_bytes(B, Hq, 1, Tk, d, split), dtype=torch.uint8, device="cuda")
         print(f"[bench] decode {name} split_keys={split}", file=sys.stderr, flush=True)
         kw = dict(scale=scale, q_offset=Tk - 1, causal=True, out=out, lse=lse)
-        _, ev_split = _timed(lambda: fa.forward_splitkv(q, k, v, split_keys=split, workspace=ws, **kw), steps, warmup)
-        _, ev_plain = _timed(lambda: fa.forward(q, k, v, **kw), steps, warmup)
+        ev_split = _timed_batch(lambda: fa.forward_splitkv(q, k, v, split_keys=split, workspace=ws, **kw), steps, warmup)
+        ev_plain = _timed_batch(lambda: fa.forward(q, k, v, **kw), steps, warmup)
         es = q.element_size()
         nbytes = es * (q.numel() + k.numel() + v.numel() + out.numel()) + 4 * lse.numel()
         gbs = nbytes / (ev_split * 1e-3) / 1e9
         res[name] = dict(split_keys=split, splitkv_us=round(ev_split * 1e3, 2), unsplit_us=round(ev_plain * 1e3, 2),
                          algorithmic_bytes=nbytes, splitkv_GBs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+        if B == 8:  # the same keys in pages of 256 keys, blocks in shuffled order, split-KV
+            bs = 256
+            nbs = Tk // bs
+            perm = torch.from_numpy(np.random.default_rng(1).permutation(B * nbs).astype(np.int32)).cuda()
+            table = perm.view(B, nbs)
+            kp = torch.empty((B * nbs, Hkv, bs, d), dtype=k.dtype, device="cuda")
+            vp = torch.empty_like(kp)
+            kp[table.long()] = k.view(B, Hkv, nbs, bs, d).transpose(1, 2)
+            vp[table.long()] = v.view(B, Hkv, nbs, bs, d).transpose(1, 2)
+            ev_paged = _timed_batch(lambda: fa.forward_paged(q, kp, vp, table, split_keys=split, workspace=ws, **kw),
+                                    steps, warmup)
+            res[name]["paged256_splitkv_us"] = round(ev_paged * 1e3, 2)
+            del kp, vp
     return res
 
 

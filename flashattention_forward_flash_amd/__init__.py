@@ -5,10 +5,11 @@ of ``csrc/fa_fwd.hip``.  PyTorch supplies device buffers and the current stream.
 no fallback: if the library is missing, importing the functions below raises.
 
 Names follow include/fa.h:
-  ``fa_fwd`` / ``fa_fwd_tiled`` / ``fa_fwd_splitkv`` / ``fa_splitkv_default_keys`` /
-  ``fa_splitkv_workspace_bytes`` / ``fa_status_str``: the C entry points over raw pointers.
-  ``forward(q, k, v, ...)``, ``forward_splitkv(q, k, v, ...)``: the same calls over torch
-  tensors (strides taken from them).
+  ``fa_fwd`` / ``fa_fwd_tiled`` / ``fa_fwd_splitkv`` / ``fa_fwd_ext`` /
+  ``fa_splitkv_default_keys`` / ``fa_splitkv_workspace_bytes`` / ``fa_status_str``: the C entry
+  points over raw pointers.
+  ``forward(q, k, v, ...)``, ``forward_splitkv(q, k, v, ...)``, ``forward_paged(q, k_pool,
+  v_pool, block_table, ...)``: the same calls over torch tensors (strides taken from them).
 """
 import ctypes
 import math
@@ -38,11 +39,22 @@ class fa_tiling(ctypes.Structure):
     _fields_ = [("rows_per_block", ctypes.c_int32), ("heads_per_block", ctypes.c_int32)]
 
 
+class fa_ext(ctypes.Structure):
+    _fields_ = [("size", ctypes.c_uint32), ("rows_per_block", ctypes.c_int32), ("heads_per_block", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("split_keys", ctypes.c_int64), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t), ("block_table", ctypes.c_void_p),
+                ("block_table_stride", ctypes.c_int64), ("block_size", ctypes.c_int64),
+                ("num_blocks", ctypes.c_int64), ("seqlens_k", ctypes.c_void_p)]
+
+    def __init__(self, **kw):
+        super().__init__(size=ctypes.sizeof(fa_ext), **kw)
+
+
 _lib = None
 _FWD_ARGS = [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int64] * 6 + [
     ctypes.c_float, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
     ctypes.POINTER(fa_strides), ctypes.c_int, ctypes.c_void_p]
-EXPORTED = ("fa_fwd", "fa_fwd_splitkv", "fa_fwd_tiled", "fa_splitkv_default_keys",
+EXPORTED = ("fa_fwd", "fa_fwd_ext", "fa_fwd_splitkv", "fa_fwd_tiled", "fa_splitkv_default_keys",
             "fa_splitkv_workspace_bytes", "fa_status_str")
 
 
@@ -63,6 +75,8 @@ def load_library(path=None):
     lib.fa_fwd_splitkv.restype = ctypes.c_int
     lib.fa_fwd_splitkv.argtypes = _FWD_ARGS + [ctypes.POINTER(fa_tiling), ctypes.c_int64, ctypes.c_void_p,
                                                ctypes.c_size_t]
+    lib.fa_fwd_ext.restype = ctypes.c_int
+    lib.fa_fwd_ext.argtypes = _FWD_ARGS + [ctypes.POINTER(fa_ext)]
     lib.fa_splitkv_default_keys.restype = ctypes.c_int64
     lib.fa_splitkv_default_keys.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int, ctypes.c_int64, ctypes.c_int]
     lib.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
@@ -98,6 +112,12 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, caus
                                           split_keys, workspace, workspace_bytes)
 
 
+def fa_fwd_ext(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, causal, window, sinks, mask, strides,
+               dtype, stream, ext):
+    return load_library().fa_fwd_ext(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, int(causal),
+                                      window, sinks, mask, strides, dtype, stream, ext)
+
+
 def fa_splitkv_default_keys(B, Hq, Hkv, Tq, Tk, q_offset=0, causal=True, window=0, dtype=FA_BF16):
     return load_library().fa_splitkv_default_keys(B, Hq, Hkv, Tq, Tk, q_offset, int(causal), window, dtype)
 
@@ -113,6 +133,16 @@ def _check(status):
 
 def forward(q, k, v, *, scale=None, q_offset=0, causal=True, window=0, sinks=None, mask=None,
             out=None, lse=None, return_lse=True, tiling=None, stream=None):
+    """O = softmax(scale * Q K^T + mask) V over torch tensors on the GPU.
+
+    q: [B, Hq, Tq, d]; k, v: [B, Hkv, Tk, d]; float32 or bfloat16, any strides with the d axis
+    contiguous (e.g. a [B, T, H, d] tensor viewed with ``.transpose(1, 2)``).  ``mask``: float32
+    tensor broadcastable to [B, Hq, Tq, Tk] (broadcast axes get stride 0).  ``sinks``: float32
+    [Hq].  ``scale`` defaults to 1/sqrt(d) rounded to fp32.  Returns (o, lse) with lse float32
+    [B, Hq, Tq] (None when ``return_lse`` is False and no ``lse`` buffer is given).
+    ``tiling``: (rows_per_block, heads_per_block) or None for automatic; results do not depend
+    on it.
+    """
     return _forward(q, k, v, scale, q_offset, causal, window, sinks, mask, out, lse, return_lse, tiling,
                     stream, None, None)
 
@@ -138,18 +168,60 @@ def forward_splitkv(q, k, v, *, split_keys=0, workspace=None, scale=None, q_offs
                     stream, int(split_keys), workspace)
 
 
-def _forward(q, k, v, scale, q_offset, causal, window, sinks, mask, out, lse, return_lse, tiling, stream,
-             split_keys, workspace):
-    """O = softmax(scale * Q K^T + mask) V over torch tensors on the GPU.
-
-    q: [B, Hq, Tq, d]; k, v: [B, Hkv, Tk, d]; float32 or bfloat16, any strides with the d axis
-    contiguous (e.g. a [B, T, H, d] tensor viewed with ``.transpose(1, 2)``).  ``mask``: float32
-    tensor broadcastable to [B, Hq, Tq, Tk] (broadcast axes get stride 0).  ``sinks``: float32
-    [Hq].  ``scale`` defaults to 1/sqrt(d) rounded to fp32.  Returns (o, lse) with lse float32
-    [B, Hq, Tq] (None when ``return_lse`` is False and no ``lse`` buffer is given).
-    ``tiling``: (rows_per_block, heads_per_block) or None for automatic; results do not depend
-    on it.
+def forward_paged(q, k_pool, v_pool, block_table, *, Tk=None, seqlens_k=None, split_keys=0, workspace=None,
+                  scale=None, q_offset=0, causal=True, window=0, sinks=None, mask=None, out=None, lse=None,
+                  return_lse=True, tiling=None, stream=None):
+    """``forward`` over paged K/V: ``k_pool``, ``v_pool`` are [num_blocks, Hkv, block_size, d] (any
+    strides, d contiguous; e.g. a [num_blocks, block_size, Hkv, d] pool viewed with
+    ``.transpose(1, 2)``), ``block_table`` int32 [B, max_blocks] on the GPU.  ``Tk``: keys per
+    sequence (default max_blocks * block_size).  ``seqlens_k``: int32 [B] per-sequence key counts
+    on the GPU; the query rows are then each sequence's last Tq positions (q_offset must be 0).
+    ``split_keys``: 0 no split, > 0 keys per split, -1 the default split (``workspace`` allocated
+    here when None).  Results equal ``forward`` on the same keys laid out contiguously.
     """
+    import torch
+    B, Hq, Tq, d = q.shape
+    nb, Hkv, bs, dk = k_pool.shape
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or dk != d:
+        raise FaError(FA_EINVAL, f"pool shapes k {tuple(k_pool.shape)} v {tuple(v_pool.shape)} d {d}")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B or (
+            block_table.numel() and block_table.stride(1) != 1):
+        raise FaError(FA_EINVAL, "block_table must be int32 [B, max_blocks] with a contiguous last axis")
+    if Tk is None:
+        Tk = block_table.shape[1] * bs
+    if seqlens_k is not None and (seqlens_k.dtype != torch.int32 or tuple(seqlens_k.shape) != (B,)
+                                  or not seqlens_k.is_contiguous()):
+        raise FaError(FA_EINVAL, "seqlens_k must be a contiguous int32 [B] tensor")
+    ext = fa_ext(block_table=block_table.data_ptr() if block_table.numel() else None,
+                 block_table_stride=block_table.stride(0) if block_table.shape[0] > 1 else block_table.shape[1],
+                 block_size=bs, num_blocks=nb,
+                 seqlens_k=seqlens_k.data_ptr() if seqlens_k is not None else None)
+    keepalive = None
+    if split_keys != 0:
+        if split_keys < 0:
+            dtype = FA_BF16 if q.dtype == torch.bfloat16 else FA_F32
+            qo = max(0, Tk - Tq) if seqlens_k is not None else int(q_offset)
+            split_keys = fa_splitkv_default_keys(B, Hq, Hkv, Tq, Tk, qo, bool(causal), int(window), dtype)
+        if workspace is None:
+            nbytes = fa_splitkv_workspace_bytes(B, Hq, Tq, Tk, d, int(split_keys)) if split_keys > 0 else 0
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+        if not workspace.is_cuda:
+            raise FaError(FA_EINVAL, "workspace must be a GPU tensor")
+        keepalive = workspace
+        ext.split_keys = int(split_keys)
+        ext.workspace = workspace.data_ptr()
+        ext.workspace_bytes = workspace.numel() * workspace.element_size()
+    if tiling is not None:
+        ext.rows_per_block, ext.heads_per_block = int(tiling[0]), int(tiling[1])
+    res = _forward(q, k_pool, v_pool, scale, q_offset, causal, window, sinks, mask, out, lse, return_lse, None,
+                   stream, None, None, ext=ext, Tk=Tk)
+    del keepalive
+    return res
+
+
+def _forward(q, k, v, scale, q_offset, causal, window, sinks, mask, out, lse, return_lse, tiling, stream,
+             split_keys, workspace, ext=None, Tk=None):
+    """Marshals the arguments of one call (strides from the tensors) and calls the library."""
     import torch
     if q.dtype == torch.float32:
         dtype = FA_F32
@@ -162,9 +234,12 @@ def _forward(q, k, v, scale, q_offset, causal, window, sinks, mask, out, lse, re
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise FaError(FA_EINVAL, "q, k, v must be 4-d [B, H, T, d]")
     B, Hq, Tq, d = q.shape
-    Bk, Hkv, Tk, dk = k.shape
-    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
-        raise FaError(FA_EINVAL, f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if ext is None:
+        Bk, Hkv, Tk, dk = k.shape
+        if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
+            raise FaError(FA_EINVAL, f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    else:
+        Hkv = k.shape[1]
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.numel() and t.stride(3) != 1:
             raise FaError(FA_EINVAL, f"{name}: the d axis must be contiguous")
@@ -211,7 +286,9 @@ def _forward(q, k, v, scale, q_offset, causal, window, sinks, mask, out, lse, re
     args = (ptr(q), ptr(k), ptr(v), ptr(out), ptr(lse), B, Hq, Hkv, Tq, Tk, d, float(scale), int(q_offset),
             bool(causal), int(window), ptr(sinks), mask_ptr, ctypes.byref(st), dtype, stream,
             ctypes.byref(til) if til is not None else None)
-    if split_keys is None:
+    if ext is not None:
+        status = fa_fwd_ext(*args[:-1], ctypes.byref(ext))
+    elif split_keys is None:
         status = fa_fwd_tiled(*args)
     else:
         if not workspace.is_cuda:

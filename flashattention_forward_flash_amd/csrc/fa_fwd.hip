@@ -33,6 +33,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 #include <type_traits>
 
 #include "fa.h"
@@ -82,7 +83,29 @@ struct Params {
   // The sink term belongs to split 0, the split that starts at key 0.
   float *ws_acc, *ws_ml;
   int32_t n_splits, split_tiles;
+  // Paged K/V ("FlashAttention forward in C", "Key Takeaways": paged attention for decode
+  // performs the same tile update on blocks).  block_table != null: k and v are pools of
+  // num_blocks blocks of block_size keys (a multiple of 64, so a tile lies in one block);
+  // key j of sequence b is row j % block_size of block block_table[b * bt_stride +
+  // j / block_size], and the (b) strides sk_b, sv_b step from block to block.
+  const int32_t *block_table;
+  int64_t bt_stride;
+  int32_t block_size, num_blocks;
+  // Per-sequence key counts (null: Tk for all): sequence b has min(seqlens_k[b], Tk) keys
+  // and its query rows are the last Tq positions, q_offset_b = keys_b - Tq.
+  const int32_t *seqlens_k;
 };
+
+// The lengths and positions of sequence b.
+__device__ __forceinline__ Params seq_params(const Params &p, int b) {
+  Params s = p;
+  if (p.seqlens_k) {
+    const int32_t n = p.seqlens_k[b];
+    s.Tk = n < 0 ? 0 : (n < p.Tk ? n : p.Tk);
+    s.q_offset = (int64_t)s.Tk - p.Tq;
+  }
+  return s;
+}
 
 // Visible keys of absolute position pos: [vis_lo, vis_hi) ("FlashAttention forward in C",
 // section 2.1, the set V_i; a window of w keys ends at pos).
@@ -229,7 +252,10 @@ struct Work {
     const int rt = p.causal ? p.n_row_tiles - 1 - rti : rti;  // heavy (late) row tiles first
     head_base = kvh * p.group + hg * p.heads_per_block;
     row0_blk = rt * p.rows_per_block;
-    // the union of the visible tiles of the workgroup's rows (lo and hi grow with the position)
+  }
+  // The union of the visible tiles of the workgroup's rows (lo and hi grow with the position),
+  // with p the parameters of sequence b.
+  __device__ __forceinline__ void set_range(const Params &p) {
     t_begin = t_end = 0;
     const int last = min(row0_blk + p.rows_per_block, p.Tq) - 1;
     const int64_t lo = vis_lo(p.q_offset + row0_blk, p), hi = vis_hi(p.q_offset + last, p);
@@ -663,15 +689,18 @@ struct Copier {
   static constexpr int ES = L::ES;
   static constexpr int BPW = L::NBLK / NW;  // 1 KiB blocks each wave copies per tensor per tile
   static_assert(L::NBLK % NW == 0, "blocks per tile must split evenly over the waves");
-  const unsigned char *kbase, *vbase;
+  const unsigned char *kbase, *vbase;  // the (b, KV head) slice, or the KV head in block 0 (paged)
   int64_t kbytes, vbytes;  // bytes of each slice from its first key to the end of key Tk - 1
+  const int32_t *bt_row;   // paged: the block-table row of sequence b
   int wid;
   uint32_t koff[BPW], voff[BPW];
 
   __device__ __forceinline__ void init(const Params &p, int b, int kvh, int wid_, int lane) {
     wid = wid_;
-    kbase = static_cast<const unsigned char *>(p.k) + ((int64_t)b * p.sk_b + (int64_t)kvh * p.sk_h) * ES;
-    vbase = static_cast<const unsigned char *>(p.v) + ((int64_t)b * p.sv_b + (int64_t)kvh * p.sv_h) * ES;
+    const int64_t bk = p.block_table ? 0 : b;
+    bt_row = p.block_table ? p.block_table + (int64_t)b * p.bt_stride : nullptr;
+    kbase = static_cast<const unsigned char *>(p.k) + (bk * p.sk_b + (int64_t)kvh * p.sk_h) * ES;
+    vbase = static_cast<const unsigned char *>(p.v) + (bk * p.sv_b + (int64_t)kvh * p.sv_h) * ES;
     kbytes = ((int64_t)(p.Tk - 1) * p.sk_t + D) * ES;
     vbytes = ((int64_t)(p.Tk - 1) * p.sv_t + D) * ES;
     const int cp_row = lane / L::CH, cp_chunk = lane % L::CH;
@@ -688,17 +717,36 @@ struct Copier {
     const int64_t skip = (int64_t)t * kBc * (IS_K ? p.sk_t : p.sv_t) * ES;
     return make_rsrc((IS_K ? kbase : vbase) + skip, (IS_K ? kbytes : vbytes) - skip);
   }
+  // Both resources of tile t.  Paged: the tile's rows in its block; rows past the sequence's
+  // keys, and a block index outside [0, num_blocks), read as zeros.
+  __device__ __forceinline__ void rsrcs(const Params &p, int t, BufRsrc &krs, BufRsrc &vrs) const {
+    if (bt_row) {
+      const uint32_t key0 = (uint32_t)t * kBc;  // < Tk < 2^31
+      const int64_t rows = min((int64_t)kBc, (int64_t)p.Tk - key0);
+      const int32_t blk = rows > 0 ? bt_row[key0 / (uint32_t)p.block_size] : -1;
+      const bool ok = blk >= 0 && blk < p.num_blocks;
+      const int64_t in_blk = key0 % (uint32_t)p.block_size;
+      const int64_t bsel = ok ? blk : 0;
+      krs = make_rsrc(kbase + (bsel * p.sk_b + in_blk * p.sk_t) * ES, ok ? ((rows - 1) * p.sk_t + D) * ES : 0);
+      vrs = make_rsrc(vbase + (bsel * p.sv_b + in_blk * p.sv_t) * ES, ok ? ((rows - 1) * p.sv_t + D) * ES : 0);
+    } else {
+      krs = rsrc<true>(p, t);
+      vrs = rsrc<false>(p, t);
+    }
+  }
   // Copy i of this wave's 2 * BPW copies of a tile: K blocks first, then V blocks.
   __device__ __forceinline__ void copy(BufRsrc krs, BufRsrc vrs, int i, unsigned char *kdst,
                                        unsigned char *vdst) const {
     if (i < BPW) buf_load_lds16(krs, kdst + (wid * BPW + i) * 1024, koff[i]);
     else buf_load_lds16(vrs, vdst + (wid * BPW + i - BPW) * 1024, voff[i - BPW]);
   }
-  template <bool IS_K>
-  __device__ __forceinline__ void tile(const Params &p, int t, unsigned char *dst) const {
-    const BufRsrc rs = rsrc<IS_K>(p, t);
+  __device__ __forceinline__ void tiles(const Params &p, int t, unsigned char *kdst, unsigned char *vdst) const {
+    BufRsrc krs, vrs;
+    rsrcs(p, t, krs, vrs);
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) buf_load_lds16(rs, dst + (wid * BPW + i) * 1024, IS_K ? koff[i] : voff[i]);
+    for (int i = 0; i < BPW; ++i) buf_load_lds16(krs, kdst + (wid * BPW + i) * 1024, koff[i]);
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) buf_load_lds16(vrs, vdst + (wid * BPW + i) * 1024, voff[i]);
   }
 };
 
@@ -711,7 +759,7 @@ struct Copier {
 // except 8-wave workgroups, which put 2 waves on each SIMD by construction.
 template <bool BF16, int D, int NW, int MODE>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((BF16 || NW == 8) ? 2 : 1)))
-fa_fwd_kernel(Params p) {
+fa_fwd_kernel(Params p0) {
   using L = Layout<BF16, D>;
   using CP = Copier<BF16, D, NW>;
   constexpr int NDS = D / 16;        // QK steps of a tile
@@ -724,7 +772,9 @@ fa_fwd_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char v1[L::TILE_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const Work wk(p);
+  Work wk(p0);
+  const Params p = seq_params(p0, wk.b);
+  wk.set_range(p);
   const int G = p.heads_per_block;
   const int head = wk.head_base + wid % G;
   Wave<BF16, D, MODE> wv;
@@ -735,7 +785,8 @@ fa_fwd_kernel(Params p) {
   auto step = [&](int t, const unsigned char *kc, const unsigned char *vc, unsigned char *kn,
                   unsigned char *vn) {
     const bool has_next = t + 1 < wk.t_end;  // the buffers kn, vn were released by the last barrier
-    const BufRsrc krs = cp.template rsrc<true>(p, t + 1), vrs = cp.template rsrc<false>(p, t + 1);
+    BufRsrc krs, vrs;
+    cp.rsrcs(p, t + 1, krs, vrs);
     auto copies = [&](int ds) {  // copy i goes with QK step i * NDS / NCP
       if (has_next) {
 #pragma unroll
@@ -755,8 +806,7 @@ fa_fwd_kernel(Params p) {
     __syncthreads();                // ... everyone's have, and buffers kc, vc are free again
   };
   if (wk.t_begin < wk.t_end) {
-    cp.template tile<true>(p, wk.t_begin, k0);
-    cp.template tile<false>(p, wk.t_begin, v0);
+    cp.tiles(p, wk.t_begin, k0, v0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
@@ -934,13 +984,17 @@ int64_t default_split_keys(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64
 
 int64_t n_splits_of(int64_t Tk, int64_t split_keys) { return std::max((int64_t)1, ceil_div(Tk, split_keys)); }
 
+// x: every optional feature, normalised (split_keys 0: no split, > 0: keys per split).
 fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
                    int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d, float scale,
                    int64_t q_offset, int causal, int64_t window, const float *sinks,
                    const float *mask, const fa_strides *strides, fa_dtype dtype, void *stream,
-                   const fa_tiling *tiling, int64_t split_keys = 0, void *workspace = nullptr,
-                   size_t workspace_bytes = 0) {
+                   const fa_ext &x) {
+  const int64_t split_keys = x.split_keys;
+  void *const workspace = x.workspace;
+  const size_t workspace_bytes = x.workspace_bytes;
   const bool split = split_keys != 0;
+  const bool paged = x.block_table != nullptr;
   // ---- arguments ----
   if (B < 0 || Hq < 0 || Hkv < 0 || Tq < 0 || Tk < 0 || q_offset < 0 || d <= 0) return FA_EINVAL;
   if (!std::isfinite(scale)) return FA_EINVAL;
@@ -956,12 +1010,28 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
       (window > 0 && window > INT64_MAX / 4))
     return FA_EUNSUPPORTED;
 
+  if (paged) {
+    if (x.block_size <= 0 || x.block_size % 64 != 0 || x.block_size > INT32_MAX / 2 || x.num_blocks < 0 ||
+        x.num_blocks > INT32_MAX || x.block_table_stride < 0 ||
+        x.block_table_stride < (Tk + x.block_size - 1) / x.block_size)
+      return FA_EINVAL;
+    if (!aligned(x.block_table, 4)) return FA_EUNSUPPORTED;
+  }
+  if (x.seqlens_k) {
+    if (q_offset != 0) return FA_EINVAL;  // positions come from the per-sequence key counts
+    if (!aligned(x.seqlens_k, 4)) return FA_EUNSUPPORTED;
+  }
+
   fa_strides s;
   if (strides) {
     s = *strides;
   } else {
     s.q[0] = Hq * Tq * d; s.q[1] = Tq * d; s.q[2] = d;
-    s.k[0] = Hkv * Tk * d; s.k[1] = Tk * d; s.k[2] = d;
+    if (paged) {  // pools [num_blocks, Hkv, block_size, d]
+      s.k[0] = Hkv * x.block_size * d; s.k[1] = x.block_size * d; s.k[2] = d;
+    } else {
+      s.k[0] = Hkv * Tk * d; s.k[1] = Tk * d; s.k[2] = d;
+    }
     s.v[0] = s.k[0]; s.v[1] = s.k[1]; s.v[2] = s.k[2];
     s.o[0] = s.q[0]; s.o[1] = s.q[1]; s.o[2] = s.q[2];
     s.lse[0] = Hq * Tq; s.lse[1] = Tq;
@@ -974,9 +1044,9 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
 
   int32_t rows_pb = 0, heads_pb = 0;
   const int64_t group = Hkv > 0 ? Hq / Hkv : 1;
-  if (tiling && (tiling->rows_per_block != 0 || tiling->heads_per_block != 0)) {
-    rows_pb = tiling->rows_per_block;
-    heads_pb = tiling->heads_per_block;
+  if (x.rows_per_block != 0 || x.heads_per_block != 0) {
+    rows_pb = x.rows_per_block;
+    heads_pb = x.heads_per_block;
     const int64_t waves32 = (int64_t)rows_pb * heads_pb;
     if (rows_pb <= 0 || heads_pb <= 0 || rows_pb % 32 != 0 || group % heads_pb != 0 ||
         (waves32 != 32 && waves32 != 64 && waves32 != 128 && waves32 != 256))
@@ -1008,9 +1078,12 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   }
   if (!aligned(lse, 4) || !aligned(sinks, 4) || !aligned(mask, 4)) return FA_EUNSUPPORTED;
 
-  // the tile copies address one (b, KV head) slice of K and of V with 32-bit offsets
-  if (Tk > 0 && (64 * s.k[2] * es >= INT32_MAX || 64 * s.v[2] * es >= INT32_MAX ||
-                 ((Tk - 1) * s.k[2] + d) * es >= INT32_MAX || ((Tk - 1) * s.v[2] + d) * es >= INT32_MAX))
+  // the tile copies address one (b, KV head) slice of K and of V (paged: one tile) with 32-bit
+  // offsets
+  if (Tk > 0 && (64 * s.k[2] * es >= INT32_MAX || 64 * s.v[2] * es >= INT32_MAX))
+    return FA_EUNSUPPORTED;
+  if (Tk > 0 && !paged &&
+      (((Tk - 1) * s.k[2] + d) * es >= INT32_MAX || ((Tk - 1) * s.v[2] + d) * es >= INT32_MAX))
     return FA_EUNSUPPORTED;
   if (rows_pb == 0) {
     if (split) split_tiling(group, Tq, &rows_pb, &heads_pb);
@@ -1048,6 +1121,11 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   p.split_tiles = split ? (int32_t)std::min(split_keys / 64, (int64_t)INT32_MAX / 4) : 0;
   p.ws_acc = split ? static_cast<float *>(workspace) : nullptr;
   p.ws_ml = split ? static_cast<float *>(workspace) + n_splits * rows_total * d : nullptr;
+  p.block_table = x.block_table;
+  p.bt_stride = paged ? x.block_table_stride : 0;
+  p.block_size = paged ? (int32_t)x.block_size : 0;
+  p.num_blocks = paged ? (int32_t)x.num_blocks : 0;
+  p.seqlens_k = x.seqlens_k;
 
   const bool bf16 = dtype == FA_BF16;
   // MODE 1 when scores need the explicit form: an additive mask, or a scale that is not
@@ -1077,8 +1155,27 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *ls
                  int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d, float scale,
                  int64_t q_offset, int causal, int64_t window, const float *sinks,
                  const float *mask, const fa_strides *strides, fa_dtype dtype, void *stream) {
+  const fa_ext x = {};
   return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, causal, window, sinks,
-                  mask, strides, dtype, stream, nullptr);
+                  mask, strides, dtype, stream, x);
+}
+
+fa_status fa_fwd_ext(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+                     int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d, float scale,
+                     int64_t q_offset, int causal, int64_t window, const float *sinks,
+                     const float *mask, const fa_strides *strides, fa_dtype dtype, void *stream,
+                     const fa_ext *ext) {
+  fa_ext x = {};
+  if (ext) {
+    if (ext->size < sizeof(uint32_t)) return FA_EINVAL;
+    std::memcpy(&x, ext, std::min((size_t)ext->size, sizeof(fa_ext)));
+  }
+  if (x.split_keys < -1) return FA_EINVAL;
+  if (x.split_keys == -1)
+    x.split_keys = default_split_keys(B, Hq, Hkv, Tq, Tk, x.seqlens_k ? std::max((int64_t)0, Tk - Tq) : q_offset,
+                                      causal, window, dtype);
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, causal, window, sinks,
+                  mask, strides, dtype, stream, x);
 }
 
 fa_status fa_fwd_tiled(const void *q, const void *k, const void *v, void *o, float *lse,
@@ -1086,8 +1183,10 @@ fa_status fa_fwd_tiled(const void *q, const void *k, const void *v, void *o, flo
                        float scale, int64_t q_offset, int causal, int64_t window,
                        const float *sinks, const float *mask, const fa_strides *strides,
                        fa_dtype dtype, void *stream, const fa_tiling *tiling) {
+  fa_ext x = {};
+  if (tiling) { x.rows_per_block = tiling->rows_per_block; x.heads_per_block = tiling->heads_per_block; }
   return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, causal, window, sinks,
-                  mask, strides, dtype, stream, tiling);
+                  mask, strides, dtype, stream, x);
 }
 
 fa_status fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
@@ -1096,10 +1195,15 @@ fa_status fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, f
                           const float *sinks, const float *mask, const fa_strides *strides,
                           fa_dtype dtype, void *stream, const fa_tiling *tiling, int64_t split_keys,
                           void *workspace, size_t workspace_bytes) {
-  if (split_keys == 0) split_keys = fa_splitkv_default_keys(B, Hq, Hkv, Tq, Tk, q_offset, causal, window, dtype);
+  if (split_keys == 0) split_keys = default_split_keys(B, Hq, Hkv, Tq, Tk, q_offset, causal, window, dtype);
   if (split_keys <= 0) return FA_EINVAL;
+  fa_ext x = {};
+  if (tiling) { x.rows_per_block = tiling->rows_per_block; x.heads_per_block = tiling->heads_per_block; }
+  x.split_keys = split_keys;
+  x.workspace = workspace;
+  x.workspace_bytes = workspace_bytes;
   return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, causal, window, sinks,
-                  mask, strides, dtype, stream, tiling, split_keys, workspace, workspace_bytes);
+                  mask, strides, dtype, stream, x);
 }
 
 int64_t fa_splitkv_default_keys(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk,

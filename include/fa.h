@@ -161,6 +161,63 @@ int64_t fa_splitkv_default_keys(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, 
 size_t fa_splitkv_workspace_bytes(int64_t B, int64_t Hq, int64_t Tq, int64_t Tk, int64_t d,
                                   int64_t split_keys);
 
+/*
+ * Optional features of fa_fwd_ext, combinable with each other and with every flag of fa_fwd.
+ * Zero-initialise the struct and set `size` to sizeof(fa_ext); a field left at zero is off.
+ *
+ * Geometry: rows_per_block, heads_per_block as in fa_tiling.
+ *
+ * Split-KV: split_keys 0 = no split; > 0 = keys per split (a multiple of 64); -1 = the
+ *   default of fa_splitkv_default_keys (for per-sequence key counts, with q_offset = Tk - Tq).
+ *   workspace and workspace_bytes as for fa_fwd_splitkv.
+ *
+ * Paged K/V ("FlashAttention forward in C", "Key Takeaways": paged attention for decode
+ *   performs the same tile update on blocks, held bit for bit to this kernel).  When
+ *   block_table is not NULL, k and v are pools of num_blocks blocks of block_size keys (a
+ *   positive multiple of 64), indexed [block, KV head, key in block, d] through strides->k
+ *   and strides->v, whose first entry then steps from block to block (strides == NULL:
+ *   contiguous [num_blocks, Hkv, block_size, d] pools).  Key j of sequence b is row
+ *   j % block_size of block block_table[b * block_table_stride + j / block_size].
+ *   block_table (device int32) needs valid entries for the blocks holding keys [0, Tk) of
+ *   each sequence (or [0, seqlens_k[b])); block_table_stride >= ceil(Tk / block_size).  A
+ *   block index outside [0, num_blocks) reads as zero keys and values (never out of
+ *   bounds).  The results equal fa_fwd's on the same keys laid out contiguously, bit for bit.
+ *
+ * Per-sequence key counts: seqlens_k (device int32 [B]) or NULL.  Sequence b then has
+ *   n_b = min(max(seqlens_k[b], 0), Tk) keys and its Tq query rows are its last Tq positions:
+ *   row i sits at p_i = n_b - Tq + i (rows with p_i < 0 see no key when causal).  q_offset
+ *   must be 0.  Row i of sequence b then equals fa_fwd with Tk = n_b and q_offset = n_b - Tq
+ *   (when that is >= 0), bit for bit.
+ */
+typedef struct {
+  uint32_t size;                  /* sizeof(fa_ext) */
+  int32_t rows_per_block;         /* launch geometry (0, 0: automatic) */
+  int32_t heads_per_block;
+  int32_t reserved;               /* 0 */
+  int64_t split_keys;             /* 0: no split; > 0: keys per split; -1: default */
+  void *workspace;                /* split-KV workspace (device) */
+  size_t workspace_bytes;
+  const int32_t *block_table;     /* paged K/V (device) or NULL */
+  int64_t block_table_stride;     /* entries between consecutive sequences' rows */
+  int64_t block_size;             /* keys per block */
+  int64_t num_blocks;             /* blocks in each pool */
+  const int32_t *seqlens_k;       /* per-sequence key counts (device) or NULL */
+} fa_ext;
+
+/*
+ * fa_fwd_ext -- fa_fwd with the optional features of `ext` (NULL: none).  Arguments as for
+ * fa_fwd; Tk is the largest key count (with paging: the logical sequence length the block
+ * table spans).  Errors as for fa_fwd, plus FA_EINVAL for an inconsistent ext (size too small,
+ * split_keys < -1 or not a multiple of 64, block_size not a positive multiple of 64,
+ * block_table_stride too short, q_offset != 0 with seqlens_k, a missing or short workspace)
+ * and FA_EUNSUPPORTED for a misaligned block table, seqlens_k or workspace.
+ */
+fa_status fa_fwd_ext(const void *q, const void *k, const void *v, void *o, float *lse,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                     float scale, int64_t q_offset, int causal, int64_t window,
+                     const float *sinks, const float *mask, const fa_strides *strides,
+                     fa_dtype dtype, void *stream, const fa_ext *ext);
+
 /* Static English name of a status code (never NULL). */
 const char *fa_status_str(fa_status s);
 

@@ -148,3 +148,61 @@ def test_splitkv_validation_errors(kw, want):
 def test_splitkv_empty_work_returns_ok_without_launch():
     assert _split_call(Tq=0) == fa.FA_OK
     assert _split_call(B=0, ws=None, ws_bytes=0) == fa.FA_OK
+
+
+def test_fa_ext_layout_matches_the_header(tmp_path):
+    """The binding's fa_ext has the C struct's size and field offsets (compiled with gcc)."""
+    fields = [f[0] for f in fa.fa_ext._fields_]
+    src = tmp_path / "ext.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "fa.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(fa_ext));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(fa_ext, {n}));\n' for n in fields) + "  return 0;\n}\n")
+    exe = tmp_path / "ext"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    want = [ctypes.sizeof(fa.fa_ext)] + [getattr(fa.fa_ext, n).offset for n in fields]
+    assert got == want
+
+
+def _ext_call(ext, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=2, Hq=4, Hkv=2, Tq=1, Tk=1000, d=64, scale=0.125, q_offset=0,
+             causal=1, window=0, sinks=None, mask=None, strides=None, dtype=fa.FA_F32, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_ext(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Tq"], a["Tk"],
+                         a["d"], a["scale"], a["q_offset"], a["causal"], a["window"], a["sinks"], a["mask"],
+                         a["strides"], a["dtype"], a["stream"], ctypes.byref(ext))
+
+
+def _paged(**kw):
+    a = dict(block_table=P, block_table_stride=16, block_size=64, num_blocks=100)
+    a.update(kw)
+    return fa.fa_ext(**a)
+
+
+@pytest.mark.parametrize("ext,kw,want", [
+    (dict(size=0), {}, fa.FA_EINVAL),                                        # size not set
+    (dict(split_keys=-2), {}, fa.FA_EINVAL),
+    (dict(split_keys=100, workspace=P, workspace_bytes=1 << 30), {}, fa.FA_EINVAL),
+    (dict(split_keys=128, workspace=None), {}, fa.FA_EINVAL),
+    (dict(paged=dict(block_size=100)), {}, fa.FA_EINVAL),                    # not a multiple of 64
+    (dict(paged=dict(block_size=0)), {}, fa.FA_EINVAL),
+    (dict(paged=dict(block_table_stride=15)), {}, fa.FA_EINVAL),             # 15 * 64 < Tk = 1000
+    (dict(paged=dict(num_blocks=-1)), {}, fa.FA_EINVAL),
+    (dict(paged=dict(block_table=P + 2)), {}, fa.FA_EUNSUPPORTED),           # misaligned block table
+    (dict(paged=dict(), seqlens_k=P), dict(q_offset=5), fa.FA_EINVAL),       # positions come from seqlens_k
+    (dict(seqlens_k=P + 1), {}, fa.FA_EUNSUPPORTED),
+    (dict(rows_per_block=48, heads_per_block=1), {}, fa.FA_EINVAL),
+    (dict(paged=dict()), dict(Hq=6, Hkv=4), fa.FA_ESHAPE),
+])
+def test_ext_validation_errors(ext, kw, want):
+    ext = dict(ext)
+    paged = ext.pop("paged", None)
+    e = _paged(**paged) if paged is not None else fa.fa_ext()
+    for n, val in ext.items():
+        setattr(e, n, val)
+    assert _ext_call(e, **kw) == want
+
+
+def test_ext_empty_work_returns_ok_without_launch():
+    assert _ext_call(_paged(), Tq=0) == fa.FA_OK
+    assert _ext_call(_paged(seqlens_k=P), B=0) == fa.FA_OK
