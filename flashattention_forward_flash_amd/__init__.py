@@ -9,7 +9,8 @@ Names follow include/fa.h:
   ``fa_splitkv_default_keys`` / ``fa_splitkv_workspace_bytes`` / ``fa_status_str``: the C entry
   points over raw pointers.
   ``forward(q, k, v, ...)``, ``forward_splitkv(q, k, v, ...)``, ``forward_paged(q, k_pool,
-  v_pool, block_table, ...)``: the same calls over torch tensors (strides taken from them).
+  v_pool, block_table, ...)``, ``forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, ...)``: the
+  same calls over torch tensors (strides taken from them).
 """
 import ctypes
 import math
@@ -44,7 +45,8 @@ class fa_ext(ctypes.Structure):
                 ("reserved", ctypes.c_int32), ("split_keys", ctypes.c_int64), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("block_table", ctypes.c_void_p),
                 ("block_table_stride", ctypes.c_int64), ("block_size", ctypes.c_int64),
-                ("num_blocks", ctypes.c_int64), ("seqlens_k", ctypes.c_void_p)]
+                ("num_blocks", ctypes.c_int64), ("seqlens_k", ctypes.c_void_p), ("cu_seqlens_q", ctypes.c_void_p),
+                ("cu_seqlens_k", ctypes.c_void_p)]
 
     def __init__(self, **kw):
         super().__init__(size=ctypes.sizeof(fa_ext), **kw)
@@ -217,6 +219,83 @@ def forward_paged(q, k_pool, v_pool, block_table, *, Tk=None, seqlens_k=None, sp
                    stream, None, None, ext=ext, Tk=Tk)
     del keepalive
     return res
+
+
+def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, scale=None, causal=True,
+                   window=0, sinks=None, out=None, lse=None, return_lse=True, split_keys=0, workspace=None,
+                   tiling=None, stream=None):
+    """Packed sequences: q [total_q, Hq, d], k, v [total_k, Hkv, d] (token and head strides free, d
+    contiguous), ``cu_seqlens_q``, ``cu_seqlens_k`` int32 [B + 1] prefix sums on the GPU,
+    ``max_seqlen_q`` / ``max_seqlen_k`` at least the longest sequence.  Row i of sequence b sits
+    at position n_b - m_b + i (its keys n_b, its rows m_b).  Returns (o [total_q, Hq, d],
+    lse [Hq, total_q]); every row equals the single-sequence ``forward`` on its own tokens.
+    ``split_keys``: 0 no split, > 0 keys per split, -1 the default (workspace allocated here
+    when None).
+    """
+    import torch
+    if q.dtype == torch.float32:
+        dtype = FA_F32
+    elif q.dtype == torch.bfloat16:
+        dtype = FA_BF16
+    else:
+        raise FaError(FA_EUNSUPPORTED, f"dtype {q.dtype} (float32 or bfloat16 only)")
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or k.shape != v.shape or k.shape[2] != q.shape[2]:
+        raise FaError(FA_EINVAL, f"packed shapes q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise FaError(FA_EINVAL, "q, k and v must share a dtype")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous() or not t.is_cuda:
+            raise FaError(FA_EINVAL, f"{name} must be a contiguous int32 GPU tensor")
+    B = cu_seqlens_q.shape[0] - 1
+    if cu_seqlens_k.shape[0] != B + 1 or B < 0:
+        raise FaError(FA_EINVAL, "cu_seqlens_q and cu_seqlens_k must both hold B + 1 entries")
+    total_q, Hq, d = q.shape
+    Hkv = k.shape[1]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.numel() and t.stride(2) != 1:
+            raise FaError(FA_EINVAL, f"{name}: the d axis must be contiguous")
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    if out is None:
+        out = torch.empty((total_q, Hq, d), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, total_q)
+                            or (lse.numel() and lse.stride(1) != 1)):
+        raise FaError(FA_EINVAL, "lse must be float32 [Hq, total_q] with a contiguous last axis")
+    st = fa_strides()
+    st.q[:] = [0, q.stride(1), q.stride(0)]
+    st.k[:] = [0, k.stride(1), k.stride(0)]
+    st.v[:] = [0, v.stride(1), v.stride(0)]
+    st.o[:] = [0, out.stride(1), out.stride(0)]
+    st.lse[:] = [0, lse.stride(0) if lse is not None else 0]
+    st.mask[:] = [0, 0, 0, 0]
+    if sinks is not None and (sinks.dtype != torch.float32 or tuple(sinks.shape) != (Hq,) or not sinks.is_contiguous()):
+        raise FaError(FA_EINVAL, "sinks must be a contiguous float32 [Hq] tensor")
+    ext = fa_ext(cu_seqlens_q=cu_seqlens_q.data_ptr(), cu_seqlens_k=cu_seqlens_k.data_ptr())
+    if tiling is not None:
+        ext.rows_per_block, ext.heads_per_block = int(tiling[0]), int(tiling[1])
+    Tq, Tk = int(max_seqlen_q), int(max_seqlen_k)
+    if split_keys != 0:
+        if split_keys < 0:
+            split_keys = fa_splitkv_default_keys(B, Hq, Hkv, Tq, Tk, max(0, Tk - Tq), bool(causal), int(window), dtype)
+        if workspace is None:
+            nbytes = fa_splitkv_workspace_bytes(B, Hq, Tq, Tk, d, int(split_keys)) if split_keys > 0 else 0
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+        ext.split_keys = int(split_keys)
+        ext.workspace = workspace.data_ptr()
+        ext.workspace_bytes = workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+
+    def ptr(t):
+        return t.data_ptr() if (t is not None and t.numel()) else None
+
+    status = fa_fwd_ext(ptr(q), ptr(k), ptr(v), ptr(out), ptr(lse), B, Hq, Hkv, Tq, Tk, d, float(scale), 0,
+                        bool(causal), int(window), ptr(sinks), None, ctypes.byref(st), dtype, stream,
+                        ctypes.byref(ext))
+    _check(status)
+    return out, lse
 
 
 def _forward(q, k, v, scale, q_offset, causal, window, sinks, mask, out, lse, return_lse, tiling, stream,

@@ -91,19 +91,36 @@ struct Params {
   const int32_t *block_table;
   int64_t bt_stride;
   int32_t block_size, num_blocks;
-  // Per-sequence key counts (null: Tk for all): sequence b has min(seqlens_k[b], Tk) keys
-  // and its query rows are the last Tq positions, q_offset_b = keys_b - Tq.
-  const int32_t *seqlens_k;
+  // Per-sequence lengths.  seqlens_k: sequence b has seqlens_k[b] keys.  Packed sequences
+  // (varlen): cu_seqlens_q / cu_seqlens_k are prefix sums over the sequences of the rows of q,
+  // o, lse / of k, v, which are then indexed by token through their t strides (the b strides
+  // are not used).  Counts are clamped to [0, Tq] and [0, Tk].  With any per-sequence length,
+  // the query rows of sequence b are its last rows: q_offset_b = keys_b - rows_b.
+  const int32_t *seqlens_k, *cu_seqlens_q, *cu_seqlens_k;
+  int32_t Tq_all;          // Tq of the call (the row stride of the split-KV workspace)
+  int64_t q_start, k_start;  // first token of this sequence in packed q, o, lse / k, v
 };
 
-// The lengths and positions of sequence b.
+__device__ __forceinline__ int32_t clamp_len(int32_t n, int32_t hi) { return n < 0 ? 0 : (n < hi ? n : hi); }
+
+// The lengths, positions and token offsets of sequence b.
 __device__ __forceinline__ Params seq_params(const Params &p, int b) {
   Params s = p;
-  if (p.seqlens_k) {
-    const int32_t n = p.seqlens_k[b];
-    s.Tk = n < 0 ? 0 : (n < p.Tk ? n : p.Tk);
-    s.q_offset = (int64_t)s.Tk - p.Tq;
+  if (p.cu_seqlens_q) {
+    const int32_t q0 = p.cu_seqlens_q[b];
+    s.Tq = clamp_len(p.cu_seqlens_q[b + 1] - q0, p.Tq);
+    s.q_start = q0;
+    s.sq_b = s.so_b = s.sl_b = 0;
   }
+  if (p.cu_seqlens_k) {
+    const int32_t k0 = p.cu_seqlens_k[b];
+    s.Tk = clamp_len(p.cu_seqlens_k[b + 1] - k0, p.Tk);
+    s.k_start = k0;
+    s.sk_b = s.sv_b = 0;
+  } else if (p.seqlens_k) {
+    s.Tk = clamp_len(p.seqlens_k[b], p.Tk);
+  }
+  if (p.seqlens_k || p.cu_seqlens_q || p.cu_seqlens_k) s.q_offset = (int64_t)s.Tk - s.Tq;
   return s;
 }
 
@@ -257,6 +274,7 @@ struct Work {
   // with p the parameters of sequence b.
   __device__ __forceinline__ void set_range(const Params &p) {
     t_begin = t_end = 0;
+    if (row0_blk >= p.Tq) return;  // a packed sequence shorter than the call's Tq
     const int last = min(row0_blk + p.rows_per_block, p.Tq) - 1;
     const int64_t lo = vis_lo(p.q_offset + row0_blk, p), hi = vis_hi(p.q_offset + last, p);
     if (hi > lo) { t_begin = (int)(lo / kBc); t_end = (int)((hi + kBc - 1) / kBc); }
@@ -316,7 +334,7 @@ struct Wave {
                : nullptr;
 
     const unsigned char *qrow = static_cast<const unsigned char *>(p.q) +
-                                ((int64_t)b * p.sq_b + (int64_t)head * p.sq_h + (int64_t)row * p.sq_t) * ES;
+                                ((int64_t)b * p.sq_b + (int64_t)head * p.sq_h + (p.q_start + row) * p.sq_t) * ES;
     if constexpr (BF16) {
 #pragma unroll
       for (int ds = 0; ds < D / 16; ++ds) {
@@ -635,7 +653,7 @@ struct Wave {
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (!row_ok) return;
     if (p.n_splits > 0) {  // split-KV: the row's state goes to the workspace as it stands
-      const int64_t r = ((int64_t)split * p.B * p.Hq + (int64_t)b * p.Hq + head) * p.Tq + row;
+      const int64_t r = ((int64_t)split * p.B * p.Hq + (int64_t)b * p.Hq + head) * p.Tq_all + row;
       float *arow = p.ws_acc + r * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -651,7 +669,7 @@ struct Wave {
       return;
     }
     unsigned char *orow = static_cast<unsigned char *>(p.o) +
-                          ((int64_t)b * p.so_b + (int64_t)head * p.so_h + (int64_t)row * p.so_t) * ES;
+                          ((int64_t)b * p.so_b + (int64_t)head * p.so_h + (p.q_start + row) * p.so_t) * ES;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -670,7 +688,7 @@ struct Wave {
         }
       }
     if (p.lse && half == 0)
-      p.lse[(int64_t)b * p.sl_b + (int64_t)head * p.sl_h + row] =
+      p.lse[(int64_t)b * p.sl_b + (int64_t)head * p.sl_h + p.q_start + row] =
           l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 };
@@ -699,8 +717,8 @@ struct Copier {
     wid = wid_;
     const int64_t bk = p.block_table ? 0 : b;
     bt_row = p.block_table ? p.block_table + (int64_t)b * p.bt_stride : nullptr;
-    kbase = static_cast<const unsigned char *>(p.k) + (bk * p.sk_b + (int64_t)kvh * p.sk_h) * ES;
-    vbase = static_cast<const unsigned char *>(p.v) + (bk * p.sv_b + (int64_t)kvh * p.sv_h) * ES;
+    kbase = static_cast<const unsigned char *>(p.k) + (bk * p.sk_b + (int64_t)kvh * p.sk_h + p.k_start * p.sk_t) * ES;
+    vbase = static_cast<const unsigned char *>(p.v) + (bk * p.sv_b + (int64_t)kvh * p.sv_h + p.k_start * p.sv_t) * ES;
     kbytes = ((int64_t)(p.Tk - 1) * p.sk_t + D) * ES;
     vbytes = ((int64_t)(p.Tk - 1) * p.sv_t + D) * ES;
     const int cp_row = lane / L::CH, cp_chunk = lane % L::CH;
@@ -826,15 +844,17 @@ fa_fwd_kernel(Params p0) {
 // With one split this is the epilogue of the unsplit kernel, bit for bit.
 // ---------------------------------------------------------------------------------------
 template <bool BF16, int D>
-__global__ __launch_bounds__(256) void fa_merge_kernel(Params p) {
+__global__ __launch_bounds__(256) void fa_merge_kernel(Params p0) {
   constexpr int EPL = D / 64;  // elements per lane
   const int lane = threadIdx.x & 63;
-  const int64_t rows = (int64_t)p.B * p.Hq * p.Tq;
+  const int64_t rows = (int64_t)p0.B * p0.Hq * p0.Tq_all;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
-  const int i = (int)(r % p.Tq);
-  const int64_t bh = r / p.Tq;
-  const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
+  const int i = (int)(r % p0.Tq_all);
+  const int64_t bh = r / p0.Tq_all;
+  const int h = (int)(bh % p0.Hq), b = (int)(bh / p0.Hq);
+  const Params p = seq_params(p0, b);
+  if (i >= p.Tq) return;  // past the rows of a packed sequence
   const f32x2 *ml = reinterpret_cast<const f32x2 *>(p.ws_ml) + r;  // split s at ml[s * rows]
 
   // M: lane s reads split s's state (64 splits at a time); the maximum is exact in any order
@@ -892,7 +912,7 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(Params p) {
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
   unsigned char *orow = static_cast<unsigned char *>(p.o) +
-                        ((int64_t)b * p.so_b + (int64_t)h * p.so_h + (int64_t)i * p.so_t) * (BF16 ? 2 : 4);
+                        ((int64_t)b * p.so_b + (int64_t)h * p.so_h + (p.q_start + i) * p.so_t) * (BF16 ? 2 : 4);
   if constexpr (BF16) {
     if constexpr (EPL == 2)
       *reinterpret_cast<uint32_t *>(orow + 4 * lane) = pack_bf16x2(a[0] * inv, a[1] * inv);
@@ -907,7 +927,7 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(Params p) {
     }
   }
   if (p.lse && lane == 0)
-    p.lse[(int64_t)b * p.sl_b + (int64_t)h * p.sl_h + i] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
+    p.lse[(int64_t)b * p.sl_b + (int64_t)h * p.sl_h + p.q_start + i] = l > 0.f ? (M + log2f(l)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1017,10 +1037,12 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
       return FA_EINVAL;
     if (!aligned(x.block_table, 4)) return FA_EUNSUPPORTED;
   }
-  if (x.seqlens_k) {
-    if (q_offset != 0) return FA_EINVAL;  // positions come from the per-sequence key counts
-    if (!aligned(x.seqlens_k, 4)) return FA_EUNSUPPORTED;
-  }
+  const bool per_seq = x.seqlens_k || x.cu_seqlens_q || x.cu_seqlens_k;
+  if (per_seq && q_offset != 0) return FA_EINVAL;  // positions come from the per-sequence lengths
+  if (x.cu_seqlens_k && (x.seqlens_k || paged)) return FA_EINVAL;  // one source of key counts
+  if ((x.cu_seqlens_q || x.cu_seqlens_k) && strides == nullptr) return FA_EINVAL;  // packed layouts
+  if (!aligned(x.seqlens_k, 4) || !aligned(x.cu_seqlens_q, 4) || !aligned(x.cu_seqlens_k, 4))
+    return FA_EUNSUPPORTED;
 
   fa_strides s;
   if (strides) {
@@ -1126,6 +1148,11 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   p.block_size = paged ? (int32_t)x.block_size : 0;
   p.num_blocks = paged ? (int32_t)x.num_blocks : 0;
   p.seqlens_k = x.seqlens_k;
+  p.cu_seqlens_q = x.cu_seqlens_q;
+  p.cu_seqlens_k = x.cu_seqlens_k;
+  p.Tq_all = (int32_t)Tq;
+  p.q_start = 0;
+  p.k_start = 0;
 
   const bool bf16 = dtype == FA_BF16;
   // MODE 1 when scores need the explicit form: an additive mask, or a scale that is not
@@ -1172,8 +1199,10 @@ fa_status fa_fwd_ext(const void *q, const void *k, const void *v, void *o, float
   }
   if (x.split_keys < -1) return FA_EINVAL;
   if (x.split_keys == -1)
-    x.split_keys = default_split_keys(B, Hq, Hkv, Tq, Tk, x.seqlens_k ? std::max((int64_t)0, Tk - Tq) : q_offset,
-                                      causal, window, dtype);
+    x.split_keys = default_split_keys(
+        B, Hq, Hkv, Tq, Tk,
+        (x.seqlens_k || x.cu_seqlens_q || x.cu_seqlens_k) ? std::max((int64_t)0, Tk - Tq) : q_offset, causal,
+        window, dtype);
   return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, causal, window, sinks,
                   mask, strides, dtype, stream, x);
 }

@@ -188,6 +188,18 @@ size_t fa_splitkv_workspace_bytes(int64_t B, int64_t Hq, int64_t Tq, int64_t Tk,
  *   row i sits at p_i = n_b - Tq + i (rows with p_i < 0 see no key when causal).  q_offset
  *   must be 0.  Row i of sequence b then equals fa_fwd with Tk = n_b and q_offset = n_b - Tq
  *   (when that is >= 0), bit for bit.
+ *
+ * Packed sequences (varlen batching: candle's B > 1 path; the batch invariance of
+ *   "FlashAttention forward in C" section 4): cu_seqlens_q and/or cu_seqlens_k (device int32
+ *   [B + 1], non-decreasing prefix sums starting at 0) or NULL.  Sequence b's query rows are
+ *   tokens [cu_seqlens_q[b], cu_seqlens_q[b + 1]) of q, o and lse (m_b of them, at most Tq),
+ *   its keys tokens [cu_seqlens_k[b], cu_seqlens_k[b + 1]) of k and v (n_b, at most Tk); the
+ *   tensors are indexed by token through the t strides and the b strides are not used (q, o:
+ *   [total_q, Hq, d] is strides {0, d, Hq d}; lse [Hq, total_q] is {0, total_q}), so strides
+ *   must be given.  Row i of sequence b sits at p_i = n_b - m_b + i (p_i = i when m_b = n_b)
+ *   and q_offset must be 0.  cu_seqlens_k excludes seqlens_k and paging (which take their key
+ *   counts from seqlens_k).  Every row equals a single-sequence fa_fwd call on its own
+ *   tokens with q_offset = n_b - m_b, bit for bit.
  */
 typedef struct {
   uint32_t size;                  /* sizeof(fa_ext) */
@@ -202,6 +214,8 @@ typedef struct {
   int64_t block_size;             /* keys per block */
   int64_t num_blocks;             /* blocks in each pool */
   const int32_t *seqlens_k;       /* per-sequence key counts (device) or NULL */
+  const int32_t *cu_seqlens_q;    /* packed query rows: prefix sums [B + 1] (device) or NULL */
+  const int32_t *cu_seqlens_k;    /* packed keys: prefix sums [B + 1] (device) or NULL */
 } fa_ext;
 
 /*
@@ -209,8 +223,9 @@ typedef struct {
  * fa_fwd; Tk is the largest key count (with paging: the logical sequence length the block
  * table spans).  Errors as for fa_fwd, plus FA_EINVAL for an inconsistent ext (size too small,
  * split_keys < -1 or not a multiple of 64, block_size not a positive multiple of 64,
- * block_table_stride too short, q_offset != 0 with seqlens_k, a missing or short workspace)
- * and FA_EUNSUPPORTED for a misaligned block table, seqlens_k or workspace.
+ * block_table_stride too short, q_offset != 0 with per-sequence lengths, cu_seqlens_k with
+ * seqlens_k or paging, packed sequences without strides, a missing or short workspace)
+ * and FA_EUNSUPPORTED for a misaligned block table, length array or workspace.
  */
 fa_status fa_fwd_ext(const void *q, const void *k, const void *v, void *o, float *lse,
                      int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,

@@ -193,6 +193,11 @@ def _paged(**kw):
     (dict(seqlens_k=P + 1), {}, fa.FA_EUNSUPPORTED),
     (dict(rows_per_block=48, heads_per_block=1), {}, fa.FA_EINVAL),
     (dict(paged=dict()), dict(Hq=6, Hkv=4), fa.FA_ESHAPE),
+    (dict(cu_seqlens_q=P), dict(q_offset=3), fa.FA_EINVAL),              # positions come from the lengths
+    (dict(cu_seqlens_q=P), {}, fa.FA_EINVAL),                            # packed layouts need strides
+    (dict(cu_seqlens_k=P, seqlens_k=P), dict(strides="bhsd"), fa.FA_EINVAL),  # two sources of key counts
+    (dict(paged=dict(), cu_seqlens_k=P), dict(strides="bhsd"), fa.FA_EINVAL),
+    (dict(cu_seqlens_q=P + 2), dict(strides="bhsd"), fa.FA_EUNSUPPORTED),
 ])
 def test_ext_validation_errors(ext, kw, want):
     ext = dict(ext)
@@ -200,6 +205,12 @@ def test_ext_validation_errors(ext, kw, want):
     e = _paged(**paged) if paged is not None else fa.fa_ext()
     for n, val in ext.items():
         setattr(e, n, val)
+    if kw.get("strides") == "bhsd":
+        st = fa.fa_strides()
+        st.q[:] = st.o[:] = [4 * 64, 64, 4 * 64]
+        st.k[:] = st.v[:] = [2 * 1000 * 64, 1000 * 64, 64]
+        st.lse[:] = [4, 1]
+        kw = dict(kw, strides=ctypes.byref(st))
     assert _ext_call(e, **kw) == want
 
 
