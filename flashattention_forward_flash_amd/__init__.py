@@ -223,14 +223,16 @@ def forward_paged(q, k_pool, v_pool, block_table, *, Tk=None, seqlens_k=None, sp
 
 def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, scale=None, causal=True,
                    window=0, sinks=None, out=None, lse=None, return_lse=True, split_keys=0, workspace=None,
-                   tiling=None, stream=None):
+                   tiling=None, stream=None, block_table=None, seqlens_k=None):
     """Packed sequences: q [total_q, Hq, d], k, v [total_k, Hkv, d] (token and head strides free, d
     contiguous), ``cu_seqlens_q``, ``cu_seqlens_k`` int32 [B + 1] prefix sums on the GPU,
     ``max_seqlen_q`` / ``max_seqlen_k`` at least the longest sequence.  Row i of sequence b sits
     at position n_b - m_b + i (its keys n_b, its rows m_b).  Returns (o [total_q, Hq, d],
     lse [Hq, total_q]); every row equals the single-sequence ``forward`` on its own tokens.
     ``split_keys``: 0 no split, > 0 keys per split, -1 the default (workspace allocated here
-    when None).
+    when None).  Paged keys: ``block_table`` int32 [B, max_blocks] with k, v pools
+    [num_blocks, Hkv, block_size, d] (as ``forward_paged``), ``cu_seqlens_k`` None and the key
+    counts from ``seqlens_k`` (int32 [B]; None: max_seqlen_k each).
     """
     import torch
     if q.dtype == torch.float32:
@@ -239,20 +241,27 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen
         dtype = FA_BF16
     else:
         raise FaError(FA_EUNSUPPORTED, f"dtype {q.dtype} (float32 or bfloat16 only)")
-    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or k.shape != v.shape or k.shape[2] != q.shape[2]:
+    paged = block_table is not None
+    kdim = 4 if paged else 3
+    if q.dim() != 3 or k.dim() != kdim or k.shape != v.shape or k.shape[-1] != q.shape[2]:
         raise FaError(FA_EINVAL, f"packed shapes q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise FaError(FA_EINVAL, "q, k and v must share a dtype")
-    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
-        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous() or not t.is_cuda:
+    if paged == (cu_seqlens_k is not None):
+        raise FaError(FA_EINVAL, "give cu_seqlens_k (packed keys) or block_table (paged keys), not both")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k), ("seqlens_k", seqlens_k),
+                    ("block_table", block_table)):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous() or not t.is_cuda):
             raise FaError(FA_EINVAL, f"{name} must be a contiguous int32 GPU tensor")
     B = cu_seqlens_q.shape[0] - 1
-    if cu_seqlens_k.shape[0] != B + 1 or B < 0:
-        raise FaError(FA_EINVAL, "cu_seqlens_q and cu_seqlens_k must both hold B + 1 entries")
+    if B < 0 or (cu_seqlens_k is not None and tuple(cu_seqlens_k.shape) != (B + 1,)) or (
+            seqlens_k is not None and tuple(seqlens_k.shape) != (B,)) or (
+            paged and (block_table.dim() != 2 or block_table.shape[0] != B)):
+        raise FaError(FA_EINVAL, "cu_seqlens_q [B + 1] with cu_seqlens_k [B + 1] or block_table [B, n] (seqlens_k [B])")
     total_q, Hq, d = q.shape
     Hkv = k.shape[1]
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.numel() and t.stride(2) != 1:
+        if t.numel() and t.stride(-1) != 1:
             raise FaError(FA_EINVAL, f"{name}: the d axis must be contiguous")
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
@@ -265,14 +274,23 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen
         raise FaError(FA_EINVAL, "lse must be float32 [Hq, total_q] with a contiguous last axis")
     st = fa_strides()
     st.q[:] = [0, q.stride(1), q.stride(0)]
-    st.k[:] = [0, k.stride(1), k.stride(0)]
-    st.v[:] = [0, v.stride(1), v.stride(0)]
+    if paged:  # pools [block, head, key in block, d]
+        st.k[:] = [k.stride(0), k.stride(1), k.stride(2)]
+        st.v[:] = [v.stride(0), v.stride(1), v.stride(2)]
+    else:
+        st.k[:] = [0, k.stride(1), k.stride(0)]
+        st.v[:] = [0, v.stride(1), v.stride(0)]
     st.o[:] = [0, out.stride(1), out.stride(0)]
     st.lse[:] = [0, lse.stride(0) if lse is not None else 0]
     st.mask[:] = [0, 0, 0, 0]
     if sinks is not None and (sinks.dtype != torch.float32 or tuple(sinks.shape) != (Hq,) or not sinks.is_contiguous()):
         raise FaError(FA_EINVAL, "sinks must be a contiguous float32 [Hq] tensor")
-    ext = fa_ext(cu_seqlens_q=cu_seqlens_q.data_ptr(), cu_seqlens_k=cu_seqlens_k.data_ptr())
+    if paged:
+        ext = fa_ext(cu_seqlens_q=cu_seqlens_q.data_ptr(), block_table=block_table.data_ptr(),
+                     block_table_stride=block_table.shape[1], block_size=k.shape[2], num_blocks=k.shape[0],
+                     seqlens_k=seqlens_k.data_ptr() if seqlens_k is not None else None)
+    else:
+        ext = fa_ext(cu_seqlens_q=cu_seqlens_q.data_ptr(), cu_seqlens_k=cu_seqlens_k.data_ptr())
     if tiling is not None:
         ext.rows_per_block, ext.heads_per_block = int(tiling[0]), int(tiling[1])
     Tq, Tk = int(max_seqlen_q), int(max_seqlen_k)

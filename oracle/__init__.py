@@ -7,8 +7,9 @@ only through the seeded inputs of ``synth``.
 ``attention()`` is a thin ctypes wrapper of ``fa_oracle.c`` (plain C, fp64, one query row
 at a time: visible scores, softmax, weighted sum of V).  The definition it follows is
 "FlashAttention forward in C" (tinyllm L9.3) section 2.1 plus the additive mask of
-"Fused attention and softmax: fast and exact" (OneModel), "What is computed"; the C source
-header lists the readings taken where the pages are silent.
+"Fused attention and softmax: fast and exact" (OneModel), "What is computed", and the softcap
+and ALiBi score variants the candle page names; the C source header lists the readings taken
+where the pages are silent.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` (worked example, closed
 forms, brute force in ``oracle/brute.py``, torch's fp64 SDPA, planted mistakes).
@@ -36,8 +37,8 @@ def _load(path=None):
             ctypes.c_void_p, i64p, ctypes.c_void_p, i64p, ctypes.c_void_p, i64p, ctypes.c_int,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_int64, ctypes.c_double, ctypes.c_int64, ctypes.c_int, ctypes.c_int64,
-            ctypes.c_void_p, ctypes.c_void_p, i64p, ctypes.c_void_p, ctypes.c_int64,
-            ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, i64p, ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
         ]
         lib.orc_set_threads.argtypes = [ctypes.c_int]
         lib.orc_set_threads.restype = None
@@ -70,13 +71,15 @@ def _as_input(a, dtype):
 
 
 def attention(q, k, v, *, scale, q_offset=0, causal=True, window=0, sinks=None, mask=None,
-              rows=None, dtype=None, threads=None, lib_path=None):
+              softcap=0.0, alibi=None, rows=None, dtype=None, threads=None, lib_path=None):
     """fp64 attention rows.
 
     q: [B, Hq, Tq, d]; k, v: [B, Hkv, Tk, d] -- numpy arrays of float64, float32, or uint16
     holding bf16 bits (``dtype=BF16``).  ``scale`` is widened exactly (pass the fp32 value the
     GPU receives).  ``mask``: None or a 4-d float32 array indexable as [b, h, i, j] (size-1 or
-    stride-0 axes broadcast).  ``sinks``: None or float32 [Hq].  ``rows``: None (all rows) or an
+    stride-0 axes broadcast).  ``sinks``: None or float32 [Hq].  ``softcap``: c > 0 turns the
+    logit into c tanh(logit / c) (0: none).  ``alibi``: None or float32 [Hq] slopes (score
+    -slope |p - j|).  ``rows``: None (all rows) or an
     int64 array [n, 3] of (b, h, i).  Returns (o, lse) in fp64: [B, Hq, Tq, d] and [B, Hq, Tq]
     for all rows, else [n, d] and [n].
     """
@@ -91,6 +94,7 @@ def attention(q, k, v, *, scale, q_offset=0, causal=True, window=0, sinks=None, 
     if Tk == 0:
         k = v = np.zeros((1, 1, 1, d), q.dtype)
     sinks_arr = None if sinks is None else np.ascontiguousarray(np.asarray(sinks, np.float32))
+    alibi_arr = None if alibi is None else np.ascontiguousarray(np.asarray(alibi, np.float32))
     mask_arr = smask = None
     if mask is not None:
         mask_arr = np.asarray(mask, np.float32)
@@ -115,7 +119,8 @@ def attention(q, k, v, *, scale, q_offset=0, causal=True, window=0, sinks=None, 
         _strides(v, 4) if Tk else sk_, dtype, B, Hq, Hkv, Tq, Tk, d, float(np.float64(scale)),
         int(q_offset), int(bool(causal)), int(window),
         None if sinks_arr is None else sinks_arr.ctypes.data,
-        None if mask_arr is None else mask_arr.ctypes.data, smask,
+        None if mask_arr is None else mask_arr.ctypes.data, smask, float(softcap),
+        None if alibi_arr is None else alibi_arr.ctypes.data,
         None if rows_arr is None else rows_arr.ctypes.data, n if rows_arr is not None else 0,
         o.ctypes.data, lse.ctypes.data)
     if rc != 0:

@@ -16,11 +16,20 @@
  *     strides (a stride of 0 broadcasts).
  *   "IV.5: Flash attention", "The reference implementation": the materialised
  *     per-head reference (scores, mask, softmax, scores @ V) that flash must match.
+ *   Score variants named by the candle page ("KV 缓存与注意力", attention/: the CPU flash
+ *   attention's variants with ALiBi and softcap), in their usual definitions:
+ *     softcap c > 0: the logit scale * q.k becomes c * tanh(scale * q.k / c);
+ *     ALiBi slopes m_h: the score gets -m_h * |p_i - j| (the distance between the
+ *     absolute positions of query and key);
+ *     s_ij = [softcap](scale * q.k) - m_h |p_i - j| + mask_ij.
  * Readings where the pages leave a step open:
  *   - the mask is indexed by (row i of this call, key j), like q;
  *   - a mask entry of -inf makes the key invisible (it counts toward "no visible key");
  *   - the sink logit z_h is raw (not multiplied by scale), one per query head;
- *   - inputs are widened exactly from fp32 (or bf16 bits) to fp64; all arithmetic fp64.
+ *   - inputs are widened exactly from fp32 (or bf16 bits) to fp64; all arithmetic fp64;
+ *   - softcap applies to the dot-product logit only; the ALiBi bias and the mask are added
+ *     after it; ALiBi uses absolute positions (p_i = q_offset + i) and |p_i - j| for keys on
+ *     either side (without causal).
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (see oracle/build.py).
  * Compile-time ORACLE_MUTANT=n plants one deliberate mistake; tests use those builds to
@@ -70,6 +79,7 @@ static int orc_visible(int64_t j, int64_t p, int causal, int64_t window) {
  *   q [B,Hq,Tq,d], k and v [B,Hkv,Tk,d] with element strides {b, h, t} and the d axis
  *   contiguous; all three in dtype (ORC_F64 / ORC_F32 / ORC_BF16 bits).
  *   sinks [Hq] fp32 or NULL; mask fp32 or NULL, element strides {b, h, i, j}.
+ *   softcap: c > 0 caps the logit, 0 = none; alibi [Hq] fp32 slopes or NULL.
  *   rows: nrows triples (b, h, i), or NULL for every row in (b, h, i) order.
  *   Outputs are compact: o_out[r * d + x], lse_out[r] for the r-th listed row.
  * Returns 0, or -1 if Hq % Hkv != 0 or an argument is out of range.
@@ -78,8 +88,8 @@ int orc_attention(const void *q, const int64_t *sq, const void *k, const int64_t
                   const void *v, const int64_t *sv, int dtype, int64_t B, int64_t Hq,
                   int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d, double scale,
                   int64_t q_offset, int causal, int64_t window, const float *sinks,
-                  const float *mask, const int64_t *smask, const int64_t *rows,
-                  int64_t nrows, double *o_out, double *lse_out) {
+                  const float *mask, const int64_t *smask, double softcap, const float *alibi,
+                  const int64_t *rows, int64_t nrows, double *o_out, double *lse_out) {
   if (B < 0 || Hq < 0 || Hkv <= 0 || Tq < 0 || Tk < 0 || d <= 0 || Hq % Hkv != 0) return -1;
   const int64_t total = rows ? nrows : B * Hq * Tq;
   const int64_t group = Hq / Hkv;
@@ -137,6 +147,24 @@ int orc_attention(const void *q, const int64_t *sq, const void *k, const int64_t
 #else
         double sc = scale * dot;
 #endif
+#if ORACLE_MUTANT != 19
+        if (softcap > 0.0) {
+#if ORACLE_MUTANT == 16 /* softcap without its outer factor */
+          sc = tanh(sc / softcap);
+#else
+          sc = softcap * tanh(sc / softcap);
+#endif
+        }
+#endif
+        if (alibi) {
+#if ORACLE_MUTANT == 17 /* ALiBi bias added with the wrong sign */
+          sc += (double)alibi[h] * fabs((double)(p - j));
+#elif ORACLE_MUTANT == 18 /* ALiBi distance from the call's row index, not the position */
+          sc -= (double)alibi[h] * fabs((double)(i - j));
+#else
+          sc -= (double)alibi[h] * fabs((double)(p - j));
+#endif
+        }
         if (mask) {
 #if ORACLE_MUTANT == 12 /* mask indexed by absolute position instead of the call's row */
           sc += (double)mask[b * smask[0] + h * smask[1] + p * smask[2] + j * smask[3]];
@@ -146,6 +174,9 @@ int orc_attention(const void *q, const int64_t *sq, const void *k, const int64_t
           sc += (double)mask[b * smask[0] + h * smask[1] + i * smask[2] + j * smask[3]];
 #endif
         }
+#if ORACLE_MUTANT == 19 /* softcap applied after the bias and the mask */
+        if (softcap > 0.0) sc = softcap * tanh(sc / softcap);
+#endif
         s[j] = sc;
         if (sc > mx) mx = sc;
       }

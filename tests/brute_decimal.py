@@ -2,7 +2,8 @@
 
 It evaluates the definition of "FlashAttention forward in C" (tinyllm L9.3), section 2.1,
 with the additive mask of "Fused attention and softmax: fast and exact" (OneModel), "What is
-computed", literally: enumerate the visible set, exponentiate every score as is (no
+computed", and the softcap / ALiBi score variants (logit c tanh(logit / c); bias
+-slope |p - j|), literally: enumerate the visible set, exponentiate every score as is (no
 max-subtraction: decimals do not overflow), sum, divide, take the log.  It is structurally
 different from the C oracle (which shifts by the row maximum in fp64) and is used only to
 pin it.
@@ -12,7 +13,16 @@ from decimal import Decimal, getcontext
 import numpy as np
 
 
-def brute_attention(q, k, v, *, scale, q_offset=0, causal=True, window=0, sinks=None, mask=None):
+def _tanh(x):
+    """tanh of a Decimal from its exponential definition."""
+    if x < 0:
+        return -_tanh(-x)
+    e = (-2 * x).exp()
+    return (1 - e) / (1 + e)
+
+
+def brute_attention(q, k, v, *, scale, q_offset=0, causal=True, window=0, sinks=None, mask=None, softcap=0.0,
+                    alibi=None):
     getcontext().prec = 50
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -34,6 +44,11 @@ def brute_attention(q, k, v, *, scale, q_offset=0, causal=True, window=0, sinks=
                 for j in visible:
                     s = sc * sum(Decimal(float(q[b, h, i, x])) * Decimal(float(k[b, kvh, j, x]))
                                  for x in range(d))
+                    if softcap > 0:
+                        c = Decimal(float(softcap))
+                        s = c * _tanh(s / c)
+                    if alibi is not None:
+                        s -= Decimal(float(np.float32(alibi[h]))) * abs(pos - j)
                     if mask is not None:
                         mv = float(mask[b, h, i, j])
                         if mv == float("-inf"):

@@ -198,14 +198,19 @@ def _brute_cases():
             for q_offset in (0, 2, 5):
                 for with_sink in (False, True):
                     for with_mask in (False, True):
-                        cases.append((causal, window, q_offset, with_sink, with_mask))
+                        cases.append((causal, window, q_offset, with_sink, with_mask, 0.0, False))
+    # the score variants: softcap, ALiBi, both, with and without the other flags
+    for ci, (softcap, alibi) in enumerate(((0.9, False), (0.0, True), (1.7, True))):
+        for causal in (False, True):
+            for q_offset, window, with_sink, with_mask in ((0, 0, False, False), (5, 3, True, True)):
+                cases.append((causal, window, q_offset, with_sink, with_mask, softcap, alibi))
     return cases
 
 
 def pin_brute_force(attn, cases=None):
     """50-digit decimal evaluation of the definition, every flag combination, tiny shapes."""
     geoms = [(1, 2, 1, 5, 9, 3), (2, 4, 2, 4, 7, 2), (1, 3, 3, 6, 6, 4)]
-    for ci, (causal, window, q_offset, with_sink, with_mask) in enumerate(cases or _brute_cases()):
+    for ci, (causal, window, q_offset, with_sink, with_mask, softcap, with_alibi) in enumerate(cases or _brute_cases()):
         B, Hq, Hkv, Tq, Tk, d = geoms[ci % len(geoms)]
         q = synth.normal_f32(synth.seed_of("pin-bf", ci, "q"), (B, Hq, Tq, d))
         k = synth.normal_f32(synth.seed_of("pin-bf", ci, "k"), (B, Hkv, Tk, d))
@@ -218,13 +223,88 @@ def pin_brute_force(attn, cases=None):
             full[synth.neg_inf_mask(synth.seed_of("pin-bf", ci, "mi"), full.shape, 0.25) == -np.inf] = -np.inf
             mask = full[:, :, :Tq]
         scale = np.float32(0.7)
-        o, lse = attn(q, k, v, scale=scale, q_offset=q_offset, causal=causal, window=window, sinks=z, mask=mask)
+        al = np.abs(synth.normal_f32(synth.seed_of("pin-bf", ci, "al"), (Hq,))) if with_alibi else None
+        extra = {}
+        if softcap:
+            extra["softcap"] = softcap
+        if with_alibi:
+            extra["alibi"] = al
+        o, lse = attn(q, k, v, scale=scale, q_offset=q_offset, causal=causal, window=window, sinks=z, mask=mask,
+                      **extra)
         ob, lb = brute_attention(q, k, v, scale=scale, q_offset=q_offset, causal=causal, window=window,
-                                 sinks=z, mask=mask)
+                                 sinks=z, mask=mask, softcap=softcap, alibi=al)
         assert np.all((lb == -np.inf) == (lse == -np.inf)), ci
         fin = np.isfinite(lb)
         assert np.max(np.abs(lse[fin] - lb[fin]) / np.maximum(1, np.abs(lb[fin])), initial=0) <= 1e-13, ci
         assert np.max(np.abs(o - ob) / np.maximum(1, np.abs(ob)), initial=0) <= 1e-13, ci
+
+
+def _geo(r, n):
+    """sum_{k<n} r^k and sum_{k<n} k r^k in closed form (0 < r < 1)."""
+    s0 = (1 - r ** n) / (1 - r)
+    s1 = r * (1 - n * r ** (n - 1) + (n - 1) * r ** n) / (1 - r) ** 2
+    return s0, s1
+
+
+def pin_alibi_closed_form(attn):
+    """q = 0 and ALiBi slope m: every dot product is 0, so the weight of key j is r^|p - j| with
+    r = e^{-m}; with v_j = (j, 1, ...) the output is a ratio of geometric sums and the lse their
+    log.  Checked at absolute positions (q_offset), with a window, and without causal (keys on
+    both sides of p)."""
+    Hq, Hkv, d = 3, 1, 2
+    slopes = np.array([0.05, 0.5, 1.25], np.float32)
+    for Tq, Tk, q_offset, causal, window in ((4, 300, 200, True, 0), (3, 300, 250, True, 40),
+                                             (5, 120, 30, False, 0), (2, 64, 0, True, 0)):
+        q = np.zeros((1, Hq, Tq, d), np.float32)
+        k = synth.normal_f32(synth.seed_of("pin-alibi", Tk, "k"), (1, Hkv, Tk, d))
+        v = np.zeros((1, Hkv, Tk, d), np.float32)
+        v[0, 0, :, 0] = np.arange(Tk)
+        v[0, 0, :, 1] = 1.0
+        o, lse = attn(q, k, v, scale=np.float32(0.5), q_offset=q_offset, causal=causal, window=window,
+                      alibi=slopes)
+        for h in range(Hq):
+            r = math.exp(-float(slopes[h]))
+            for i in range(Tq):
+                p = q_offset + i
+                hi = min(Tk - 1, p) if causal else Tk - 1        # last visible key
+                lo = max(0, p - window + 1) if window > 0 else 0  # first visible key
+                # keys at or left of p: distances 0 .. p - lo (only those <= hi); right of p: 1 .. hi - p
+                nl = min(p, hi) - lo + 1
+                sl0, sl1 = _geo(r, nl)
+                dl = p - min(p, hi)                               # distance of the nearest left key
+                nr = max(0, hi - p)
+                sr0, sr1 = _geo(r, nr)
+                # left keys j = p - dl - t (t = 0 .. nl-1), weight r^(dl + t); right keys j = p + 1 + t, weight r^(1 + t)
+                w_l, wj_l = r ** dl * sl0, r ** dl * ((p - dl) * sl0 - sl1)
+                w_r, wj_r = r * sr0, r * ((p + 1) * sr0 + sr1)
+                den = w_l + w_r
+                assert abs(o[0, h, i, 0] - (wj_l + wj_r) / den) <= 1e-9 * max(1.0, p), (h, i, causal)
+                assert abs(o[0, h, i, 1] - 1.0) <= 1e-12
+                assert abs(lse[0, h, i] - math.log(den)) <= 1e-12, (h, i)
+
+
+def pin_softcap_saturation(attn):
+    """Softcap c: a key whose logit is huge scores exactly c (tanh saturates), a key with a zero
+    dot product scores 0 plus its mask entry m; with one-hot values the output is
+    sigmoid(c - m) and the lse ln(e^c + e^m).  The same keys without softcap keep the raw logit."""
+    c, m = 2.0, 1.5
+    q = np.array([[[[1.0, 0.0]]]], np.float32)
+    k = np.array([[[[1.0e6, 0.0], [0.0, 1.0]]]], np.float32)
+    v = np.array([[[[1.0, 0.0], [0.0, 1.0]]]], np.float32)
+    mask = np.array([[[[0.0, m]]]], np.float32)
+    o, lse = attn(q, k, v, scale=np.float32(1.0), causal=False, mask=mask, softcap=c)
+    sig = 1.0 / (1.0 + math.exp(-(c - m)))
+    assert abs(o[0, 0, 0, 0] - sig) <= 1e-14 and abs(o[0, 0, 0, 1] - (1 - sig)) <= 1e-14
+    assert abs(lse[0, 0, 0] - math.log(math.exp(c) + math.exp(m))) <= 1e-14
+    # a logit far below the cap is nearly unchanged: c tanh(x / c) = x - x^3 / (3 c^2) + ...
+    x = 0.01
+    q2 = np.array([[[[x, 0.0]]]], np.float32)
+    k2 = np.array([[[[1.0, 0.0], [0.0, 0.0]]]], np.float32)
+    o2, lse2 = attn(q2, k2, v, scale=np.float32(1.0), causal=False, softcap=c)
+    xs = float(np.float32(x))
+    s0 = c * math.tanh(xs / c)
+    assert abs(s0 - (xs - xs ** 3 / (3 * c * c))) <= 1e-10
+    assert abs(lse2[0, 0, 0] - math.log(math.exp(s0) + 1.0)) <= 1e-14
 
 
 def pin_sdpa(attn):
@@ -313,6 +393,7 @@ def pin_streamed_equals_materialised(attn):
             assert np.max(np.abs(lse[fin] - ls_[fin]), initial=0) <= 1e-12
 
 
-ALL_PINS = [pin_hand_example, pin_sinks, pin_no_visible_key, pin_closed_form_q_zero,
+ALL_PINS = [pin_hand_example, pin_sinks, pin_no_visible_key, pin_closed_form_q_zero, pin_alibi_closed_form,
+            pin_softcap_saturation,
             pin_closed_form_q_zero_mask, pin_const_v, pin_single_visible_key, pin_mask_shift,
             pin_brute_force, pin_sdpa, pin_streamed_equals_materialised]

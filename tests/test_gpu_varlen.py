@@ -105,3 +105,33 @@ def test_varlen_rows_at_the_end(dtype, split):
     klens = [100, 1, 700, 10, 2000, 64]
     _check(qlens, klens, 8, 2, 128, dtype, True, 0, True, split, f"tail/{split}")
     _check(qlens, klens, 8, 2, 128, dtype, True, 256, False, split, f"tail-window/{split}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("split", [0, 192])
+def test_varlen_queries_over_paged_keys(dtype, split):
+    """Packed query rows over a paged KV cache (per-sequence key counts from seqlens_k): equal to
+    the same call with the keys packed contiguously, bit for bit."""
+    from test_gpu_paged import _page
+    qlens, klens = [5, 1, 30, 1, 64], [100, 1, 700, 2000, 64]
+    Hq, Hkv, d, bs = 8, 2, 128, 128
+    q, k, v, gq, gk, gv = _packed(f"vpaged/{dtype}", qlens, klens, Hq, Hkv, d, dtype)
+    Tk = max(klens)
+    # the same keys per sequence, padded to Tk and paged
+    kpad = torch.zeros((len(klens), Hkv, Tk, d), dtype=gk.dtype, device="cuda")
+    vpad = torch.zeros_like(kpad)
+    k0 = 0
+    for b, n in enumerate(klens):
+        kpad[b, :, :n] = gk[k0:k0 + n].transpose(0, 1)
+        vpad[b, :, :n] = gv[k0:k0 + n].transpose(0, 1)
+        k0 += n
+    kp, vp, table = _page(kpad, vpad, bs, seed=9)
+    seqlens = torch.tensor(klens, dtype=torch.int32, device="cuda")
+    sc = scale_for(d)
+    say("varlen over paged keys", dtype, split)
+    o1, l1 = fa.forward_varlen(gq, gk, gv, _cu(qlens), _cu(klens), max(qlens), Tk, scale=sc, causal=True,
+                               split_keys=split)
+    o2, l2 = fa.forward_varlen(gq, kp, vp, _cu(qlens), None, max(qlens), Tk, scale=sc, causal=True,
+                               split_keys=split, block_table=table, seqlens_k=seqlens)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o1), bits(o2)) and np.array_equal(bits(l1), bits(l2))

@@ -30,6 +30,10 @@ MUTANTS = {
     13: "mask subtracted",
     14: "wrong sign in the exponent",
     15: "value operand read transposed",
+    16: "softcap without its outer factor",
+    17: "ALiBi bias with the wrong sign",
+    18: "ALiBi distance from the row index instead of the position",
+    19: "softcap applied after the bias and the mask",
 }
 
 
