@@ -46,7 +46,8 @@ class fa_ext(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t), ("block_table", ctypes.c_void_p),
                 ("block_table_stride", ctypes.c_int64), ("block_size", ctypes.c_int64),
                 ("num_blocks", ctypes.c_int64), ("seqlens_k", ctypes.c_void_p), ("cu_seqlens_q", ctypes.c_void_p),
-                ("cu_seqlens_k", ctypes.c_void_p)]
+                ("cu_seqlens_k", ctypes.c_void_p), ("softcap", ctypes.c_float), ("reserved2", ctypes.c_int32),
+                ("alibi_slopes", ctypes.c_void_p)]
 
     def __init__(self, **kw):
         super().__init__(size=ctypes.sizeof(fa_ext), **kw)
@@ -134,7 +135,7 @@ def _check(status):
 
 
 def forward(q, k, v, *, scale=None, q_offset=0, causal=True, window=0, sinks=None, mask=None,
-            out=None, lse=None, return_lse=True, tiling=None, stream=None):
+            out=None, lse=None, return_lse=True, tiling=None, stream=None, softcap=0.0, alibi_slopes=None):
     """O = softmax(scale * Q K^T + mask) V over torch tensors on the GPU.
 
     q: [B, Hq, Tq, d]; k, v: [B, Hkv, Tk, d]; float32 or bfloat16, any strides with the d axis
@@ -143,14 +144,16 @@ def forward(q, k, v, *, scale=None, q_offset=0, causal=True, window=0, sinks=Non
     [Hq].  ``scale`` defaults to 1/sqrt(d) rounded to fp32.  Returns (o, lse) with lse float32
     [B, Hq, Tq] (None when ``return_lse`` is False and no ``lse`` buffer is given).
     ``tiling``: (rows_per_block, heads_per_block) or None for automatic; results do not depend
-    on it.
+    on it.  ``softcap``: c > 0 caps the logit as c tanh(logit / c); ``alibi_slopes``: float32
+    [Hq] slopes adding -slope |p_i - j| to the score.
     """
     return _forward(q, k, v, scale, q_offset, causal, window, sinks, mask, out, lse, return_lse, tiling,
-                    stream, None, None)
+                    stream, None, None, ext=_variants(None, softcap, alibi_slopes, tiling, q))
 
 
 def forward_splitkv(q, k, v, *, split_keys=0, workspace=None, scale=None, q_offset=0, causal=True, window=0,
-                    sinks=None, mask=None, out=None, lse=None, return_lse=True, tiling=None, stream=None):
+                    sinks=None, mask=None, out=None, lse=None, return_lse=True, tiling=None, stream=None,
+                    softcap=0.0, alibi_slopes=None):
     """``forward`` with the keys cut into splits of ``split_keys`` keys (a multiple of 64; 0 picks
     ``fa_splitkv_default_keys``), the splits run in parallel and merged per row (split-KV /
     Flash-Decoding).  ``workspace``: a GPU tensor of at least ``fa_splitkv_workspace_bytes``
@@ -166,13 +169,18 @@ def forward_splitkv(q, k, v, *, split_keys=0, workspace=None, scale=None, q_offs
     if workspace is None:
         nbytes = fa_splitkv_workspace_bytes(B, Hq, Tq, Tk, d, int(split_keys)) if split_keys > 0 else 0
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    ext = _variants(None, softcap, alibi_slopes, tiling, q)
+    if ext is not None:
+        ext.split_keys = int(split_keys)
+        ext.workspace = workspace.data_ptr()
+        ext.workspace_bytes = workspace.numel() * workspace.element_size()
     return _forward(q, k, v, scale, q_offset, causal, window, sinks, mask, out, lse, return_lse, tiling,
-                    stream, int(split_keys), workspace)
+                    stream, int(split_keys), workspace, ext=ext)
 
 
 def forward_paged(q, k_pool, v_pool, block_table, *, Tk=None, seqlens_k=None, split_keys=0, workspace=None,
                   scale=None, q_offset=0, causal=True, window=0, sinks=None, mask=None, out=None, lse=None,
-                  return_lse=True, tiling=None, stream=None):
+                  return_lse=True, tiling=None, stream=None, softcap=0.0, alibi_slopes=None):
     """``forward`` over paged K/V: ``k_pool``, ``v_pool`` are [num_blocks, Hkv, block_size, d] (any
     strides, d contiguous; e.g. a [num_blocks, block_size, Hkv, d] pool viewed with
     ``.transpose(1, 2)``), ``block_table`` int32 [B, max_blocks] on the GPU.  ``Tk``: keys per
@@ -213,8 +221,7 @@ def forward_paged(q, k_pool, v_pool, block_table, *, Tk=None, seqlens_k=None, sp
         ext.split_keys = int(split_keys)
         ext.workspace = workspace.data_ptr()
         ext.workspace_bytes = workspace.numel() * workspace.element_size()
-    if tiling is not None:
-        ext.rows_per_block, ext.heads_per_block = int(tiling[0]), int(tiling[1])
+    _variants(ext, softcap, alibi_slopes, tiling, q)
     res = _forward(q, k_pool, v_pool, scale, q_offset, causal, window, sinks, mask, out, lse, return_lse, None,
                    stream, None, None, ext=ext, Tk=Tk)
     del keepalive
@@ -223,7 +230,7 @@ def forward_paged(q, k_pool, v_pool, block_table, *, Tk=None, seqlens_k=None, sp
 
 def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, scale=None, causal=True,
                    window=0, sinks=None, out=None, lse=None, return_lse=True, split_keys=0, workspace=None,
-                   tiling=None, stream=None, block_table=None, seqlens_k=None):
+                   tiling=None, stream=None, block_table=None, seqlens_k=None, softcap=0.0, alibi_slopes=None):
     """Packed sequences: q [total_q, Hq, d], k, v [total_k, Hkv, d] (token and head strides free, d
     contiguous), ``cu_seqlens_q``, ``cu_seqlens_k`` int32 [B + 1] prefix sums on the GPU,
     ``max_seqlen_q`` / ``max_seqlen_k`` at least the longest sequence.  Row i of sequence b sits
@@ -291,8 +298,7 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen
                      seqlens_k=seqlens_k.data_ptr() if seqlens_k is not None else None)
     else:
         ext = fa_ext(cu_seqlens_q=cu_seqlens_q.data_ptr(), cu_seqlens_k=cu_seqlens_k.data_ptr())
-    if tiling is not None:
-        ext.rows_per_block, ext.heads_per_block = int(tiling[0]), int(tiling[1])
+    _variants(ext, softcap, alibi_slopes, tiling, q)
     Tq, Tk = int(max_seqlen_q), int(max_seqlen_k)
     if split_keys != 0:
         if split_keys < 0:
@@ -316,6 +322,25 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen
     return out, lse
 
 
+def _variants(ext, softcap, alibi_slopes, tiling, q):
+    """Puts the score variants and the tiling into `ext` (made when needed); returns it, or None
+    when there is neither an ext nor a variant."""
+    import torch
+    if ext is None and not softcap and alibi_slopes is None:
+        return None
+    if ext is None:
+        ext = fa_ext()
+    if tiling is not None:
+        ext.rows_per_block, ext.heads_per_block = int(tiling[0]), int(tiling[1])
+    ext.softcap = float(softcap)
+    if alibi_slopes is not None:
+        if (alibi_slopes.dtype != torch.float32 or alibi_slopes.dim() != 1 or not alibi_slopes.is_contiguous()
+                or not alibi_slopes.is_cuda or alibi_slopes.shape[0] != q.shape[-3 if q.dim() == 4 else 1]):
+            raise FaError(FA_EINVAL, "alibi_slopes must be a contiguous float32 [Hq] GPU tensor")
+        ext.alibi_slopes = alibi_slopes.data_ptr()
+    return ext
+
+
 def _forward(q, k, v, scale, q_offset, causal, window, sinks, mask, out, lse, return_lse, tiling, stream,
              split_keys, workspace, ext=None, Tk=None):
     """Marshals the arguments of one call (strides from the tensors) and calls the library."""
@@ -331,8 +356,9 @@ def _forward(q, k, v, scale, q_offset, causal, window, sinks, mask, out, lse, re
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise FaError(FA_EINVAL, "q, k, v must be 4-d [B, H, T, d]")
     B, Hq, Tq, d = q.shape
-    if ext is None:
-        Bk, Hkv, Tk, dk = k.shape
+    if ext is None or not ext.block_table:
+        Bk, Hkv, Tk_, dk = k.shape
+        Tk = Tk_ if Tk is None else Tk
         if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
             raise FaError(FA_EINVAL, f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
     else:

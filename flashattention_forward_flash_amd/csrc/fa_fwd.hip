@@ -98,6 +98,11 @@ struct Params {
   // the query rows of sequence b are its last rows: q_offset_b = keys_b - rows_b.
   const int32_t *seqlens_k, *cu_seqlens_q, *cu_seqlens_k;
   int32_t Tq_all;          // Tq of the call (the row stride of the split-KV workspace)
+  // Score variants (the candle page's flash attention offers softcap and ALiBi): softcap c > 0
+  // turns the logit x = scale q.k into c tanh(x / c); ALiBi adds -slope_h |p_i - j|.  Kernels
+  // of MODE 2 apply them: cap_in = scale / c, cap_out = c log2(e) (0: no softcap).
+  float cap_in, cap_out;
+  const float *alibi;      // [Hq] slopes or null
   int64_t q_start, k_start;  // first token of this sequence in packed q, o, lse / k, v
 };
 
@@ -137,6 +142,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const uint32_t lo = __builtin_bit_cast(unsigned short, (__bf16)a);
   const uint32_t hi = __builtin_bit_cast(unsigned short, (__bf16)b);
   return lo | (hi << 16);
+}
+
+// tanh(u) for the softcap: the odd Taylor series through u^13 for |u| < 0.55 (truncation
+// < 4e-7 relative), 1 - 2 / (e^{2|u|} + 1) above (hardware exp2 and reciprocal; saturates to
+// 1), with the sign of u.
+__device__ __forceinline__ float tanh_f(float u) {
+  const float a = fabsf(u);
+  const float a2 = a * a;
+  float poly = 21844.f / 6081075.f;
+  poly = __builtin_fmaf(poly, a2, -1382.f / 155925.f);
+  poly = __builtin_fmaf(poly, a2, 62.f / 2835.f);
+  poly = __builtin_fmaf(poly, a2, -17.f / 315.f);
+  poly = __builtin_fmaf(poly, a2, 2.f / 15.f);
+  poly = __builtin_fmaf(poly, a2, -1.f / 3.f);
+  poly = __builtin_fmaf(poly * a2, a, a);
+  const float e = __builtin_amdgcn_exp2f(a * (2.f * kLog2e));
+  const float big = 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
+  return copysignf(a < 0.55f ? poly : big, u);
 }
 
 // Maps the launch index to a work index so that consecutive work items (which share a KV
@@ -301,6 +324,8 @@ struct Wave {
   int w_begin, w_end;        // tiles holding any key visible to the wave's rows
   int64_t full_lo, full_hi;  // tiles inside [full_lo, full_hi) are visible to all its rows
   const float *mrow;
+  float al_slope;            // MODE 2: -slope_h log2(e) (0 without ALiBi)
+  int64_t pos;               // MODE 2: the row's absolute position
   bf16x8 qb[BF16 ? D / 16 : 1];
   float qf[BF16 ? 1 : D / 2];
   float m_run, l_run;        // reference maximum (base-2 units) and this half's partial l
@@ -329,7 +354,11 @@ struct Wave {
     // clamped to [0, Tk] so they fit 32 bits
     r_hi = row_ok ? (int)vis_hi(p.q_offset + row, p) : 0;
     r_lo = row_ok ? (int)min(vis_lo(p.q_offset + row, p), (int64_t)r_hi) : 0;
-    mrow = MODE == 1 && p.mask
+    if constexpr (MODE == 2) {
+      al_slope = p.alibi ? -p.alibi[head] * kLog2e : 0.f;
+      pos = p.q_offset + row;
+    }
+    mrow = MODE != 0 && p.mask
                ? p.mask + (int64_t)b * p.sm_b + (int64_t)head * p.sm_h + (int64_t)row * p.sm_i
                : nullptr;
 
@@ -458,8 +487,10 @@ struct Wave {
   //   them (scaling by a positive constant commutes with max and with fp32 rounding) and each
   //   weight is exp2(fma(s, scale log2 e, -m)).
   // MODE 1 (additive mask, or scale <= 0): x = fma(s, scale log2 e, mask log2 e).
+  // MODE 2 (softcap or ALiBi): x = [c log2 e tanh(s scale / c) | s scale log2 e]
+  //   + dist (-slope log2 e) + mask log2 e.
   __device__ __forceinline__ void scores(const Params &p, int t, f32x16 (&sc)[2]) const {
-    if constexpr (MODE == 1) {
+    if constexpr (MODE != 0) {
       float mv[2][16];
       if (mrow && p.mask_vec && t * kBc + kBc <= p.Tk) {
         // registers 4g..4g+3 of a block hold 4 consecutive keys: one 16-byte read
@@ -481,10 +512,25 @@ struct Wave {
             mv[kb][i] = (mrow && row_ok && key < p.Tk) ? mrow[(int64_t)key * p.sm_j] : 0.f;
           }
       }
+      if constexpr (MODE == 1) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sc[kb][i] = __builtin_fmaf(sc[kb][i], p.scale_log2, mv[kb][i] * kLog2e);
+          for (int i = 0; i < 16; ++i) sc[kb][i] = __builtin_fmaf(sc[kb][i], p.scale_log2, mv[kb][i] * kLog2e);
+      } else {
+        const bool cap = p.cap_out > 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = t * kBc + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+            const int64_t dd = pos - key;
+            const float dist = (float)(dd < 0 ? -dd : dd);
+            float x = cap ? tanh_f(sc[kb][i] * p.cap_in) * p.cap_out : sc[kb][i] * p.scale_log2;
+            x = __builtin_fmaf(dist, al_slope, x);
+            sc[kb][i] = x + mv[kb][i] * kLog2e;
+          }
+      }
     }
   }
   // Keys this row cannot see become -inf by select (a no-op on tiles that are `full`).
@@ -938,7 +984,7 @@ typedef void (*KernelFn)(Params);
 
 template <bool BF16, int D, int NW>
 KernelFn pick_mode(int mode) {
-  return mode ? fa_fwd_kernel<BF16, D, NW, 1> : fa_fwd_kernel<BF16, D, NW, 0>;
+  return mode == 2 ? fa_fwd_kernel<BF16, D, NW, 2> : mode ? fa_fwd_kernel<BF16, D, NW, 1> : fa_fwd_kernel<BF16, D, NW, 0>;
 }
 
 template <bool BF16, int D>
@@ -1037,6 +1083,8 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
       return FA_EINVAL;
     if (!aligned(x.block_table, 4)) return FA_EUNSUPPORTED;
   }
+  if (!(x.softcap >= 0.f) || std::isinf(x.softcap)) return FA_EINVAL;  // NaN, negative or infinite cap
+  if (!aligned(x.alibi_slopes, 4)) return FA_EUNSUPPORTED;
   const bool per_seq = x.seqlens_k || x.cu_seqlens_q || x.cu_seqlens_k;
   if (per_seq && q_offset != 0) return FA_EINVAL;  // positions come from the per-sequence lengths
   if (x.cu_seqlens_k && (x.seqlens_k || paged)) return FA_EINVAL;  // one source of key counts
@@ -1151,13 +1199,16 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   p.cu_seqlens_q = x.cu_seqlens_q;
   p.cu_seqlens_k = x.cu_seqlens_k;
   p.Tq_all = (int32_t)Tq;
+  p.cap_in = x.softcap > 0.f ? scale / x.softcap : 0.f;
+  p.cap_out = x.softcap > 0.f ? x.softcap * kLog2e : 0.f;
+  p.alibi = x.alibi_slopes;
   p.q_start = 0;
   p.k_start = 0;
 
   const bool bf16 = dtype == FA_BF16;
   // MODE 1 when scores need the explicit form: an additive mask, or a scale that is not
   // positive (the raw-maximum shortcut needs scale > 0).
-  const int mode = (mask != nullptr || !(scale > 0.f)) ? 1 : 0;
+  const int mode = (x.softcap > 0.f || x.alibi_slopes) ? 2 : (mask != nullptr || !(scale > 0.f)) ? 1 : 0;
   KernelFn fn = bf16 ? (d == 64 ? pick_nw<true, 64>(nw, mode) : pick_nw<true, 128>(nw, mode))
                      : (d == 64 ? pick_nw<false, 64>(nw, mode) : pick_nw<false, 128>(nw, mode));
   (void)hipGetLastError();  // clear a stale error so the check below reports this launch

@@ -200,6 +200,14 @@ size_t fa_splitkv_workspace_bytes(int64_t B, int64_t Hq, int64_t Tq, int64_t Tk,
  *   and q_offset must be 0.  cu_seqlens_k excludes seqlens_k and paging (which take their key
  *   counts from seqlens_k).  Every row equals a single-sequence fa_fwd call on its own
  *   tokens with q_offset = n_b - m_b, bit for bit.
+ *
+ * Score variants (the candle page, "KV 缓存与注意力", attention/: variants with ALiBi and
+ *   softcap; their usual definitions): softcap c > 0 turns the logit x = scale * q.k into
+ *   c * tanh(x / c) (0: off; negative, NaN or infinite: FA_EINVAL); alibi_slopes (device fp32
+ *   [Hq] or NULL) adds -slope_h * |p_i - j| to the score, p_i the row's absolute position (the
+ *   distance counts keys on either side).  The score becomes
+ *     s_ij = [c tanh(scale q_i.k_j / c)] - slope_h |p_i - j| + mask[b, h, i, j].
+ *   Both keep every property above (chunking, tiling, batch, paging, split-KV).
  */
 typedef struct {
   uint32_t size;                  /* sizeof(fa_ext) */
@@ -216,6 +224,9 @@ typedef struct {
   const int32_t *seqlens_k;       /* per-sequence key counts (device) or NULL */
   const int32_t *cu_seqlens_q;    /* packed query rows: prefix sums [B + 1] (device) or NULL */
   const int32_t *cu_seqlens_k;    /* packed keys: prefix sums [B + 1] (device) or NULL */
+  float softcap;                  /* logit cap c > 0, or 0 for none */
+  int32_t reserved2;              /* 0 */
+  const float *alibi_slopes;      /* [Hq] fp32 ALiBi slopes (device) or NULL */
 } fa_ext;
 
 /*

@@ -198,6 +198,10 @@ def _paged(**kw):
     (dict(cu_seqlens_k=P, seqlens_k=P), dict(strides="bhsd"), fa.FA_EINVAL),  # two sources of key counts
     (dict(paged=dict(), cu_seqlens_k=P), dict(strides="bhsd"), fa.FA_EINVAL),
     (dict(cu_seqlens_q=P + 2), dict(strides="bhsd"), fa.FA_EUNSUPPORTED),
+    (dict(softcap=-1.0), {}, fa.FA_EINVAL),
+    (dict(softcap=float("nan")), {}, fa.FA_EINVAL),
+    (dict(softcap=float("inf")), {}, fa.FA_EINVAL),
+    (dict(alibi_slopes=P + 2), {}, fa.FA_EUNSUPPORTED),
 ])
 def test_ext_validation_errors(ext, kw, want):
     ext = dict(ext)
