@@ -138,6 +138,26 @@ __device__ __forceinline__ int64_t vis_lo(int64_t pos, const Params &p) {
   return p.window > 0 ? (pos - p.window + 1 > 0 ? pos - p.window + 1 : 0) : 0;
 }
 
+// Split-KV: the key splits [s_lo, s_hi) that meet the visible keys of position pos, and
+// whether that is a single split that alone makes the row's result (with a sink, only split 0
+// can: it holds the sink).  Such a row is finished by its split's work item like an unsplit
+// row (the merge of one split with weight 2^0 = 1 is the same arithmetic); the others are
+// merged.
+struct SplitSpan {
+  int s_lo, s_hi;
+  bool single;
+  __device__ __forceinline__ SplitSpan(int64_t pos, const Params &p) {
+    const int64_t lo = vis_lo(pos, p), hi = vis_hi(pos, p);  // both in [0, Tk]
+    const uint32_t kps = (uint32_t)p.split_tiles * 64u;
+    s_lo = s_hi = 0;
+    if (hi > lo) {
+      s_lo = (int)((uint32_t)lo / kps);
+      s_hi = (int)((uint32_t)(hi - 1) / kps) + 1;
+    }
+    single = s_hi == s_lo + 1 && (p.sinks == nullptr || s_lo == 0);
+  }
+};
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const uint32_t lo = __builtin_bit_cast(unsigned short, (__bf16)a);
   const uint32_t hi = __builtin_bit_cast(unsigned short, (__bf16)b);
@@ -698,7 +718,11 @@ struct Wave {
   __device__ __forceinline__ void finish(const Params &p, int b, int head, int split) {
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (!row_ok) return;
-    if (p.n_splits > 0) {  // split-KV: the row's state goes to the workspace as it stands
+    if (p.n_splits > 0) {
+      const SplitSpan span(p.q_offset + row, p);
+      if (span.single) {
+        if (split != span.s_lo) return;  // nothing of this row here; its split writes o and lse
+      } else {  // split-KV: the row's state goes to the workspace as it stands, for the merge
       const int64_t r = ((int64_t)split * p.B * p.Hq + (int64_t)b * p.Hq + head) * p.Tq_all + row;
       float *arow = p.ws_acc + r * D;
 #pragma unroll
@@ -713,6 +737,7 @@ struct Wave {
         *reinterpret_cast<f32x2 *>(p.ws_ml + 2 * r) = ml;
       }
       return;
+      }
     }
     unsigned char *orow = static_cast<unsigned char *>(p.o) +
                           ((int64_t)b * p.so_b + (int64_t)head * p.so_h + (p.q_start + row) * p.so_t) * ES;
@@ -839,6 +864,9 @@ fa_fwd_kernel(Params p0) {
   Work wk(p0);
   const Params p = seq_params(p0, wk.b);
   wk.set_range(p);
+  // split-KV: no row of this work item sees a key of its split, so the merge reads none of its
+  // states (split 0 keeps the sink term and always writes them)
+  if (p.n_splits > 0 && wk.t_begin >= wk.t_end && (wk.split != 0 || p.sinks == nullptr)) return;
   const int G = p.heads_per_block;
   const int head = wk.head_base + wid % G;
   Wave<BF16, D, MODE> wv;
@@ -883,7 +911,9 @@ fa_fwd_kernel(Params p0) {
 
 // ---------------------------------------------------------------------------------------
 // Split-KV merge ("FlashAttention forward in C", "Going further": the partial (m, l, a) of
-// the key splits are combined with the same rescale as the tiles).  One wave per query row:
+// the key splits are combined with the same rescale as the tiles).  One wave per query row
+// that sees more than one split, over the splits that meet the row's visible keys (and split 0
+// with a sink; the states of other splits were never written):
 //   M = max of m_s over the splits with l_s > 0
 //   l = sum_s 2^(m_s - M) l_s,  a = sum_s 2^(m_s - M) a_s      (s ascending, fixed order)
 //   o = l > 0 ? a * (1 / l) : 0,  lse = l > 0 ? (M + log2 l) ln 2 : -inf
@@ -893,53 +923,61 @@ template <bool BF16, int D>
 __global__ __launch_bounds__(256) void fa_merge_kernel(Params p0) {
   constexpr int EPL = D / 64;  // elements per lane
   const int lane = threadIdx.x & 63;
+  // grid (ceil(Tq / 4), Hq, B): wave w of block x takes row 4 x + w of head y of sequence z
   const int64_t rows = (int64_t)p0.B * p0.Hq * p0.Tq_all;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  const int i = (int)(r % p0.Tq_all);
-  const int64_t bh = r / p0.Tq_all;
-  const int h = (int)(bh % p0.Hq), b = (int)(bh / p0.Hq);
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6), h = blockIdx.y, b = blockIdx.z;
+  if (i >= p0.Tq_all) return;
+  const int64_t r = ((int64_t)b * p0.Hq + h) * p0.Tq_all + i;
   const Params p = seq_params(p0, b);
   if (i >= p.Tq) return;  // past the rows of a packed sequence
+  const SplitSpan span(p.q_offset + i, p);
+  if (span.single) return;  // finished by its split's work item
   const f32x2 *ml = reinterpret_cast<const f32x2 *>(p.ws_ml) + r;  // split s at ml[s * rows]
 
-  // M: lane s reads split s's state (64 splits at a time); the maximum is exact in any order
+  // The splits read: those meeting the row's visible keys, and split 0 when it holds the sink
+  // (the states of other splits were never written); the k-th, k < ns, in ascending order.
+  int s_lo = span.s_lo, s_hi = span.s_hi;
+  const bool with0 = p.sinks && s_lo > 0;
+  if (p.sinks && s_hi == 0) s_hi = 1;
+  const int ns = s_hi - s_lo + (with0 ? 1 : 0);
+  auto split_of = [&](int k) { return with0 ? (k == 0 ? 0 : s_lo + k - 1) : s_lo + k; };
+  auto bcast = [](float x, int k) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), k)); };
+
+  // M: lane k reads the k-th split's state (64 at a time); the maximum is exact in any order
   float M = -INFINITY;
-  for (int s = lane; s < p.n_splits; s += 64) {
-    const f32x2 st = ml[(int64_t)s * rows];
-    if (st[1] > 0.f) M = fmaxf(M, st[0]);
+  for (int k0 = 0; k0 < ns; k0 += 64) {
+    float mk = -INFINITY;
+    if (k0 + lane < ns) {
+      const f32x2 st = ml[(int64_t)split_of(k0 + lane) * rows];
+      if (st[1] > 0.f) mk = st[0];
+    }
+    const int n = min(64, ns - k0);
+    for (int k = 0; k < n; ++k) M = fmaxf(M, bcast(mk, k));
   }
-#pragma unroll
-  for (int x = 1; x < 64; x <<= 1) M = fmaxf(M, __shfl_xor(M, x));
 
   // l and a summed over the splits in ascending order; split s has weight w_s = 2^(m_s - M),
-  // 0 when it saw no key.  Lane s computes w_s, and every lane takes the weights in order.
+  // 0 when it saw no key.  Lane k computes w_k; every lane takes the weights in order.
   float l = 0.f, a[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) a[e] = 0.f;
-  for (int s0 = 0; s0 < p.n_splits; s0 += 64) {
+  for (int k0 = 0; k0 < ns; k0 += 64) {
     float w = 0.f, ls = 0.f;
-    if (s0 + lane < p.n_splits) {
-      const f32x2 st = ml[(int64_t)(s0 + lane) * rows];
+    if (k0 + lane < ns) {
+      const f32x2 st = ml[(int64_t)split_of(k0 + lane) * rows];
       if (st[1] > 0.f) { w = __builtin_amdgcn_exp2f(st[0] - M); ls = st[1]; }
     }
-    const int n = min(64, p.n_splits - s0);
+    const int n = min(64, ns - k0);
     for (int j0 = 0; j0 < n; j0 += 8) {  // 8 splits' accumulator loads in flight at a time
       float wj[8], lj[8], v[8][EPL];
-      bool any = false;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        wj[j] = __shfl(w, (j0 + j) & 63);
-        lj[j] = __shfl(ls, (j0 + j) & 63);
-        if (j0 + j >= n) wj[j] = 0.f;
-        any |= wj[j] > 0.f;
+        wj[j] = j0 + j < n ? bcast(w, j0 + j) : 0.f;
+        lj[j] = j0 + j < n ? bcast(ls, j0 + j) : 0.f;
       }
-      if (!any) continue;  // splits that saw no key of this row add nothing
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int s = s0 + j0 + j;
-        if (j0 + j < n) {
-          const float *as = p.ws_acc + ((int64_t)s * rows + r) * D + EPL * lane;
+        if (wj[j] > 0.f) {
+          const float *as = p.ws_acc + ((int64_t)split_of(k0 + j0 + j) * rows + r) * D + EPL * lane;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) v[j][e] = as[e];
         } else {
@@ -949,7 +987,7 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(Params p0) {
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        if (!(wj[j] > 0.f)) continue;
+        if (!(wj[j] > 0.f)) continue;  // splits that saw no key of this row add nothing
         l = l + wj[j] * lj[j];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) a[e] = a[e] + wj[j] * v[j][e];
@@ -1162,7 +1200,8 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   const int nw = (int)((int64_t)rows_pb * heads_pb / 32);
   const int64_t n_row_tiles = (Tq + rows_pb - 1) / rows_pb;
   const int64_t n_blocks = B * Hkv * (group / heads_pb) * n_row_tiles * (split ? n_splits : 1);
-  if (n_blocks > INT32_MAX || (split && rows_total / 4 + 1 > INT32_MAX)) return FA_EUNSUPPORTED;
+  // the merge grid is (ceil(Tq / 4), Hq, B)
+  if (n_blocks > INT32_MAX || (split && (Hq > 65535 || B > 65535))) return FA_EUNSUPPORTED;
 
   Params p;
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.sinks = sinks; p.mask = mask;
@@ -1218,7 +1257,7 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   if (split) {  // merge the splits' row states into o and lse (same stream, so after the above)
     void (*merge)(Params) = bf16 ? (d == 64 ? fa_merge_kernel<true, 64> : fa_merge_kernel<true, 128>)
                                  : (d == 64 ? fa_merge_kernel<false, 64> : fa_merge_kernel<false, 128>);
-    hipLaunchKernelGGL(merge, dim3((unsigned)((rows_total + 3) / 4)), dim3(256), 0,
+    hipLaunchKernelGGL(merge, dim3((unsigned)((Tq + 3) / 4), (unsigned)Hq, (unsigned)B), dim3(256), 0,
                        static_cast<hipStream_t>(stream), p);
     if (hipGetLastError() != hipSuccess) return FA_EDEVICE;
   }

@@ -137,7 +137,9 @@ fa_status fa_fwd_tiled(const void *q, const void *k, const void *v, void *o, flo
  *                    FA_EINVAL; misaligned: FA_EUNSUPPORTED).  Its contents on entry do not
  *                    matter; it holds the per-split row states afterwards.  Calls that
  *                    overlap in time need workspaces of their own.
- * Both kernels are enqueued on `stream`; the library allocates nothing.
+ * Both kernels are enqueued on `stream`; the library allocates nothing.  B and Hq must be at
+ * most 65,535 (else FA_EUNSUPPORTED).  A row whose visible keys lie in one split (and, with
+ * a sink, in split 0) is finished by that split's kernel; only the others go through the merge.
  */
 fa_status fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
                          int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
