@@ -9,7 +9,9 @@ The same JSON line also reports
   * roofline: the kernel's average duration from HIP events on its stream, against the
     MI355X dense bf16 MFMA peak;
   * prefill_ms: 28 back-to-back calls (one per layer, fresh seeded inputs per layer) at
-    16 query / 8 KV heads, d 128: 511 tokens fp32, 2044 tokens fp32 and bf16;
+    16 query / 8 KV heads, d 128: 511 tokens fp32, 2044 tokens fp32 and bf16; and
+    prefill_ms_splitkv: the same through split-KV at the default split size (results within
+    tolerance of the plain call, still invariant to query chunking at that split size);
   * extra workloads: the 32/8-head d 64 sliding-window (512) prefill with sinks, chunked
     (1000, 1000, 1000, 1096) and whole, the non-causal run with a broadcast additive mask, and
     decode (one query row, split-KV and unsplit) at 8 x 32/8 heads x 8,192 keys bf16 and at
@@ -153,8 +155,9 @@ def bench_mask_run(h, steps, warmup):
     return dict(ms=ev, tflops=flops / (ev * 1e-3) / 1e12)
 
 
-def bench_prefill(T, dtype, layers=28, reps=5):
-    """28 calls (one per layer) at 16/8 heads, d 128, in the concatenated-heads layout."""
+def bench_prefill(T, dtype, layers=28, reps=5, split=False):
+    """28 calls (one per layer) at 16/8 heads, d 128, in the concatenated-heads layout; with
+    `split`, through split-KV at the default split size (one workspace for all layers)."""
     import torch
     import flashattention_forward_flash_amd as fa
     Hq, Hkv, d = 16, 8, 128
@@ -164,16 +167,26 @@ def bench_prefill(T, dtype, layers=28, reps=5):
             for _ in range(layers)]
     scale = float(np.float32(1 / math.sqrt(d)))
 
+    sk = fa.fa_splitkv_default_keys(1, Hq, Hkv, T, T, 0, True, 0, fa.FA_BF16 if dtype == "bf16" else fa.FA_F32)
+    ws = torch.empty(fa.fa_splitkv_workspace_bytes(1, Hq, T, T, d, sk), dtype=torch.uint8, device="cuda")
+
     def run_all():
         for (q, k, v), o in zip(per_layer, outs):
-            fa.forward(q, k, v, scale=scale, causal=True, out=o, return_lse=False)
+            if split:
+                fa.forward_splitkv(q, k, v, split_keys=sk, workspace=ws, scale=scale, causal=True, out=o,
+                                   return_lse=False)
+            else:
+                fa.forward(q, k, v, scale=scale, causal=True, out=o, return_lse=False)
 
-    print(f"[bench] prefill T={T} {dtype} x{layers} layers", file=sys.stderr, flush=True)
+    print(f"[bench] prefill T={T} {dtype} x{layers} layers{' split-KV' if split else ''}", file=sys.stderr, flush=True)
     wall, ev = _timed(run_all, reps, 2)
     flops = 4.0 * d * Hq * visible_pairs(T, T) * layers
     peak = PEAK_F32_TFLOPS if dtype == "f32" else PEAK_BF16_TFLOPS
-    return dict(ms=round(ev, 4), per_call_ms=round(ev / layers, 5), tflops=round(flops / (ev * 1e-3) / 1e12, 2),
-                frac_peak=round(flops / (ev * 1e-3) / 1e12 / peak, 4))
+    res = dict(ms=round(ev, 4), per_call_ms=round(ev / layers, 5), tflops=round(flops / (ev * 1e-3) / 1e12, 2),
+               frac_peak=round(flops / (ev * 1e-3) / 1e12 / peak, 4))
+    if split:
+        res["split_keys"] = int(sk)
+    return res
 
 
 def bench_window_chunks(steps=10, warmup=3):
@@ -351,6 +364,11 @@ def main():
             "511_f32_28L": bench_prefill(511, "f32"),
             "2044_f32_28L": bench_prefill(2044, "f32"),
             "2044_bf16_28L": bench_prefill(2044, "bf16"),
+        }
+        result["prefill_ms_splitkv"] = {
+            "511_f32_28L": bench_prefill(511, "f32", split=True),
+            "2044_f32_28L": bench_prefill(2044, "f32", split=True),
+            "2044_bf16_28L": bench_prefill(2044, "bf16", split=True),
         }
         result["window_sinks_4096"] = bench_window_chunks()
         result["decode"] = bench_decode()
