@@ -15,7 +15,9 @@ The same JSON line also reports
   * extra workloads: the 32/8-head d 64 sliding-window (512) prefill with sinks, chunked
     (1000, 1000, 1000, 1096) and whole, the non-causal run with a broadcast additive mask, and
     decode (one query row, split-KV and unsplit) at 8 x 32/8 heads x 8,192 keys bf16 and at
-    9/3 heads d 64 fp32 with 1,024 and 4,096 keys;
+    9/3 heads d 64 fp32 with 1,024 and 4,096 keys; a packed varlen batch of 8 mixed-length
+    prefills against one call per sequence; the softcap / ALiBi score variants at 32/8 heads,
+    8,192 tokens;
   * cpu_baseline: the fp64 oracle timed on the host cores over a bounded row sample of the
     headline workload.
 """
@@ -276,6 +278,62 @@ def bench_decode(steps=50, warmup=10):
     return res
 
 
+def bench_varlen(steps=10, warmup=3):
+    """Packed batch of 8 causal self-attention prefills of mixed lengths (16/8 heads, d 128,
+    bf16) in one call, against one call per sequence."""
+    import torch
+    import synth
+    import flashattention_forward_flash_amd as fa
+    lens = [2044, 511, 1024, 100, 2044, 300, 1500, 777]
+    Hq, Hkv, d = 16, 8, 128
+    tot = sum(lens)
+    q = _dev(synth.normal(synth.seed_of("varlen", "q"), (tot, Hq, d), "bf16"))
+    k = _dev(synth.normal(synth.seed_of("varlen", "k"), (tot, Hkv, d), "bf16"))
+    v = _dev(synth.normal(synth.seed_of("varlen", "v"), (tot, Hkv, d), "bf16"))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((Hq, tot), dtype=torch.float32, device="cuda")
+    scale = float(np.float32(1 / math.sqrt(d)))
+    print("[bench] varlen packed batch", file=sys.stderr, flush=True)
+    packed = _timed_batch(lambda: fa.forward_varlen(q, k, v, cu, cu, max(lens), max(lens), scale=scale, causal=True,
+                                                   out=out, lse=lse), steps, warmup)
+    views = []
+    s0 = 0
+    for n in lens:
+        views.append(tuple(t[s0:s0 + n].transpose(0, 1)[None] for t in (q, k, v, out)))
+        s0 += n
+
+    def per_seq():
+        for qs, ks, vs, os_ in views:
+            fa.forward(qs, ks, vs, scale=scale, causal=True, out=os_, return_lse=False)
+
+    separate = _timed_batch(per_seq, steps, warmup)
+    flops = 4.0 * d * Hq * sum(visible_pairs(n, n) for n in lens)
+    return dict(lengths=lens, packed_ms=round(packed, 4), per_sequence_calls_ms=round(separate, 4),
+                packed_tflops=round(flops / (packed * 1e-3) / 1e12, 2))
+
+
+def bench_variants(steps=10, warmup=3):
+    """Score variants at B=1, 32/8 heads, T=8192, d 128, bf16, causal: the plain call, softcap
+    30, ALiBi (slopes 2^(-8(h+1)/32)) and both; TFLOP/s over causal-visible pairs."""
+    import torch
+    import flashattention_forward_flash_amd as fa
+    B, Hq, Hkv, T, d = 1, 32, 8, 8192, 128
+    q, k, v = _inputs("variants", B, Hq, Hkv, T, T, d, "bf16")
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+    scale = float(np.float32(1 / math.sqrt(d)))
+    slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / Hq) for h in range(Hq)], dtype=torch.float32, device="cuda")
+    flops = 4.0 * d * B * Hq * visible_pairs(T, T)
+    res = {}
+    for name, kw in (("plain", {}), ("softcap30", dict(softcap=30.0)), ("alibi", dict(alibi_slopes=slopes)),
+                     ("softcap30_alibi", dict(softcap=30.0, alibi_slopes=slopes))):
+        print(f"[bench] variants {name}", file=sys.stderr, flush=True)
+        ms = _timed_batch(lambda: fa.forward(q, k, v, scale=scale, causal=True, out=out, lse=lse, **kw), steps, warmup)
+        res[name] = dict(ms=round(ms, 4), tflops=round(flops / (ms * 1e-3) / 1e12, 2))
+    return res
+
+
 def cpu_baseline(h, target_s=15.0):
     """The fp64 oracle on the host cores over a seeded row sample of the headline workload,
     scaled to the metric's unit (TFLOP/s over the sampled rows' visible pairs)."""
@@ -372,6 +430,8 @@ def main():
         }
         result["window_sinks_4096"] = bench_window_chunks()
         result["decode"] = bench_decode()
+        result["varlen_batch"] = bench_varlen()
+        result["score_variants"] = bench_variants()
     if not args.no_cpu and not args.headline_only:
         result["cpu_baseline"] = cpu_baseline(h)
     print(json.dumps(result), flush=True)

@@ -510,6 +510,10 @@ struct Wave {
   // MODE 2 (softcap or ALiBi): x = [c log2 e tanh(s scale / c) | s scale log2 e]
   //   + dist (-slope log2 e) + mask log2 e.
   __device__ __forceinline__ void scores(const Params &p, int t, f32x16 (&sc)[2]) const {
+    if constexpr (MODE == 2) {
+      variants(p, t, sc);
+      if (!p.mask) return;
+    }
     if constexpr (MODE != 0) {
       float mv[2][16];
       if (mrow && p.mask_vec && t * kBc + kBc <= p.Tk) {
@@ -538,19 +542,32 @@ struct Wave {
 #pragma unroll
           for (int i = 0; i < 16; ++i) sc[kb][i] = __builtin_fmaf(sc[kb][i], p.scale_log2, mv[kb][i] * kLog2e);
       } else {
-        const bool cap = p.cap_out > 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = t * kBc + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-            const int64_t dd = pos - key;
-            const float dist = (float)(dd < 0 ? -dd : dd);
-            float x = cap ? tanh_f(sc[kb][i] * p.cap_in) * p.cap_out : sc[kb][i] * p.scale_log2;
-            x = __builtin_fmaf(dist, al_slope, x);
-            sc[kb][i] = x + mv[kb][i] * kLog2e;
-          }
+          for (int i = 0; i < 16; ++i) sc[kb][i] = sc[kb][i] + mv[kb][i] * kLog2e;
       }
+    }
+  }
+  // MODE 2 before the mask: the capped logit and the ALiBi bias.  The distance |p - key| is
+  // |(p - 64 t) - offset| in fp32, exact for distances below 2^24 (the offset of register i is
+  // the key's place in the tile).
+  __device__ __forceinline__ void variants(const Params &p, int t, f32x16 (&sc)[2]) const {
+    const float d0 = (float)(pos - (int64_t)t * kBc);
+    auto biased = [&](float x, int kb, int i) {
+      const float off = (float)(kb * 32 + 8 * (i >> 2) + (i & 3)) + (half ? 4.f : 0.f);
+      return __builtin_fmaf(fabsf(d0 - off), al_slope, x);
+    };
+    if (p.cap_out > 0.f) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[kb][i] = biased(tanh_f(sc[kb][i] * p.cap_in) * p.cap_out, kb, i);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[kb][i] = biased(sc[kb][i] * p.scale_log2, kb, i);
     }
   }
   // Keys this row cannot see become -inf by select (a no-op on tiles that are `full`).
@@ -844,10 +861,12 @@ struct Copier {
 // the other pair of LDS buffers while the current one is used, its copies spread over the QK
 // steps of the current tile.
 // ---------------------------------------------------------------------------------------
-// bf16 kernels are built for 2 waves per SIMD; fp32 ones (matrix-bound, larger tiles) for 1,
-// except 8-wave workgroups, which put 2 waves on each SIMD by construction.
+// bf16 kernels are built for 2 waves per SIMD; fp32 ones (matrix-bound, larger tiles) and the
+// score variants (MODE 2, whose extra registers would spill at 2) for 1, except 8-wave
+// workgroups, which put 2 waves on each SIMD by construction.
 template <bool BF16, int D, int NW, int MODE>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((BF16 || NW == 8) ? 2 : 1)))
+__global__ void __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(MODE == 2 ? (NW == 8 ? 2 : 1) : (BF16 || NW == 8) ? 2 : 1)))
 fa_fwd_kernel(Params p0) {
   using L = Layout<BF16, D>;
   using CP = Copier<BF16, D, NW>;
