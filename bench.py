@@ -19,7 +19,8 @@ The same JSON line also reports
     prefills against one call per sequence; the softcap / ALiBi score variants at 32/8 heads,
     8,192 tokens;
   * cpu_baseline: the fp64 oracle timed on the host cores over a bounded row sample of the
-    headline workload.
+    headline workload;
+  * sclk_during_headline: the shader clock rocm-smi reports while the headline kernel runs.
 """
 import argparse
 import hashlib
@@ -334,6 +335,42 @@ def bench_variants(steps=10, warmup=3):
     return res
 
 
+def sample_sclk(h, seconds=2.0):
+    """The shader clock while the headline kernel runs back to back: `rocm-smi --showclocks`
+    polled from a host thread (MHz values seen; None where rocm-smi is unavailable)."""
+    import subprocess
+    import threading
+    import torch
+    import flashattention_forward_flash_amd as fa
+    seen, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                                     timeout=10).stdout
+                m = re.search(r'"sclk clock speed:": "\((\d+)Mhz\)"', out)
+                if m:
+                    seen.append(int(m.group(1)))
+            except (OSError, subprocess.SubprocessError):
+                return
+            stop.wait(0.3)
+
+    out = torch.empty_like(h["q"])
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            fa.forward(h["q"], h["k"], h["v"], scale=h["scale"], causal=True, out=out, return_lse=False)
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    if not seen:
+        return None
+    return dict(mhz_samples=seen, mhz_median=float(np.median(seen)))
+
+
 def cpu_baseline(h, target_s=15.0):
     """The fp64 oracle on the host cores over a seeded row sample of the headline workload,
     scaled to the metric's unit (TFLOP/s over the sampled rows' visible pairs)."""
@@ -413,6 +450,10 @@ def main():
         "kernel_ms": round(h["event_ms"], 4),
         "algorithmic_bytes": h["bytes"],
     }
+    clk = sample_sclk(h)
+    result["sclk_during_headline"] = clk
+    if clk:  # the published peak assumes 2.4 GHz; the same fraction at the clock the box ran at
+        result["frac_mfma_peak_at_measured_sclk"] = round(achieved / (PEAK_BF16_TFLOPS * clk["mhz_median"] / 2400.0), 4)
     if not args.headline_only:
         m = bench_mask_run(h, max(3, args.steps // 4), 2)
         result["mask_run"] = {"ms": round(m["ms"], 4), "tflops": round(m["tflops"], 2),
