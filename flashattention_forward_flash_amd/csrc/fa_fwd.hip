@@ -22,12 +22,19 @@
 //    next MFMA once keys are permuted consistently), and the per-row rescale alpha is
 //    lane-local.  For bf16, V stays row-major in LDS and each lane gathers its V^T operand
 //    with transposing LDS reads (ds_read_b64_tr_b16).
-//  * Online softmax in base 2: x = s * scale * log2(e); p = exp2(x - m) on the hardware exp2;
-//    alpha = exp2(m_old - m_new), taken as exactly 1 when the maximum does not move and as
-//    0 when m_old = -inf (the guards of "Fused attention and softmax", exact definition
-//    steps 2 and 5); lse = (m + log2 l) ln 2.
+//  * Online softmax in base 2: x = s * scale * log2(e); p = exp2(x - m) on the hardware exp2.
+//    The reference point m moves only when a tile's maximum exceeds it by more than kLazy;
+//    alpha = exp2(m_old - m_new) is then exactly 1 when m does not move and 0 when m_old =
+//    -inf (the guards of "Fused attention and softmax", exact definition steps 2 and 5);
+//    lse = (m + log2 l) ln 2.
 //  * Compiled with -ffp-contract=off: every fused multiply-add is written out, so the same
 //    source line gives the same bits on every code path (boundary or interior tile).
+//  * The same kernel serves split-KV (a work item per query tile and key split, its row
+//    states merged by fa_merge_kernel), paged K/V (each tile's rows found through a block
+//    table), packed sequences and per-sequence lengths (seq_params): they change which tiles
+//    a work item visits and where a tile is read from, never the arithmetic of a row.
+//  * Kernels: MODE 0 (no mask, scale > 0: raw-maximum shortcut), MODE 1 (additive mask or
+//    scale <= 0: explicit scores), MODE 2 (softcap / ALiBi score variants).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -74,7 +81,9 @@ struct Params {
   int32_t causal;
   int32_t mask_vec;        // mask rows contiguous and 16-byte aligned: read 4 entries at a time
   int32_t tile_major;      // order work query-tile-major (a mask shared by every (b, h))
+  int32_t mask_lds;        // MODE 1: each tile's 32 x 64 mask block is staged in LDS (MaskCopier)
   float scale_log2;        // scale * log2(e)
+  float scale;             // scale (MODE 1 scores are scale q.k + mask, in natural units)
   // Split-KV ("FlashAttention forward in C", "Going further": split-KV / Flash-Decoding).
   // n_splits = 0: no split, rows end in o and lse.  Otherwise key split s is the absolute key
   // range [64 s split_tiles, 64 (s + 1) split_tiles); a work item covers one split and writes
@@ -344,6 +353,7 @@ struct Wave {
   int w_begin, w_end;        // tiles holding any key visible to the wave's rows
   int64_t full_lo, full_hi;  // tiles inside [full_lo, full_hi) are visible to all its rows
   const float *mrow;
+  uint32_t mask_lds_row;     // MODE 1 with a staged mask: this row's place in the LDS block
   float al_slope;            // MODE 2: -slope_h log2(e) (0 without ALiBi)
   int64_t pos;               // MODE 2: the row's absolute position
   bf16x8 qb[BF16 ? D / 16 : 1];
@@ -506,17 +516,32 @@ struct Wave {
   // MODE 0 (no mask, scale > 0): the scores stay raw dot products; the row maximum is taken on
   //   them (scaling by a positive constant commutes with max and with fp32 rounding) and each
   //   weight is exp2(fma(s, scale log2 e, -m)).
-  // MODE 1 (additive mask, or scale <= 0): x = fma(s, scale log2 e, mask log2 e).
+  // MODE 1 (additive mask, or scale <= 0): y = fma(s, scale, mask) in natural units; the
+  //   row maximum is taken on y and each weight is exp2(fma(y, log2 e, -m)).
   // MODE 2 (softcap or ALiBi): x = [c log2 e tanh(s scale / c) | s scale log2 e]
   //   + dist (-slope log2 e) + mask log2 e.
-  __device__ __forceinline__ void scores(const Params &p, int t, f32x16 (&sc)[2]) const {
+  __device__ __forceinline__ void scores(const Params &p, int t, f32x16 (&sc)[2],
+                                        const unsigned char *ml) const {
     if constexpr (MODE == 2) {
       variants(p, t, sc);
       if (!p.mask) return;
     }
     if constexpr (MODE != 0) {
       float mv[2][16];
-      if (mrow && p.mask_vec && t * kBc + kBc <= p.Tk) {
+      if (MODE == 1 && p.mask_lds) {
+        // the row's 64 entries of the staged block: logical 16-byte chunk c of LDS row r sits at
+        // chunk c ^ (r % 16); registers 4g..4g+3 of key block kb are chunk 8 kb + 2 g + half
+        const uint32_t r = mask_lds_row;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const uint32_t c = (uint32_t)(kb * 8 + 2 * g + half) ^ (r & 15u);
+            const f32x4 m4 = *reinterpret_cast<const f32x4 *>(ml + r * 256u + c * 16u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mv[kb][4 * g + e] = m4[e];
+          }
+      } else if (mrow && p.mask_vec && t * kBc + kBc <= p.Tk) {
         // registers 4g..4g+3 of a block hold 4 consecutive keys: one 16-byte read
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -540,7 +565,7 @@ struct Wave {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sc[kb][i] = __builtin_fmaf(sc[kb][i], p.scale_log2, mv[kb][i] * kLog2e);
+          for (int i = 0; i < 16; ++i) sc[kb][i] = __builtin_fmaf(sc[kb][i], p.scale, mv[kb][i]);
       } else {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -590,7 +615,9 @@ struct Wave {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
-    if constexpr (MODE == 0) mx = mx * p.scale_log2;  // -inf stays -inf (scale > 0)
+    // to base-2 units (a positive factor commutes with max and with fp32 rounding; -inf stays)
+    if constexpr (MODE == 0) mx = mx * p.scale_log2;
+    if constexpr (MODE == 1) mx = mx * kLog2e;
     // The reference point m moves only when this tile's maximum exceeds it by more than
     // kLazy (base-2 units), or m is still -inf: weights are then exp2(x - m) <= 2^kLazy, and
     // most tiles need no rescale.  The rule depends on the row's own scores only, so a row's
@@ -613,6 +640,8 @@ struct Wave {
       for (int i = 0; i < 16; ++i) {
         if constexpr (MODE == 0)
           w[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i], p.scale_log2, -shift));
+        else if constexpr (MODE == 1)
+          w[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i], kLog2e, -shift));
         else
           w[kb][i] = __builtin_amdgcn_exp2f(sc[kb][i] - shift);
       }
@@ -652,8 +681,8 @@ struct Wave {
   }
 
   // The whole online-softmax step of tile t on `sacc`.
-  __device__ __forceinline__ void softmax(const Params &p, int t) {
-    scores(p, t, sacc);
+  __device__ __forceinline__ void softmax(const Params &p, int t, const unsigned char *ml = nullptr) {
+    scores(p, t, sacc, ml);
     if (!full(t)) select(t, sacc);
     rescale(weights(p, sacc));
   }
@@ -857,6 +886,41 @@ struct Copier {
 };
 
 // ---------------------------------------------------------------------------------------
+// Mask tiles through LDS (MODE 1 when the workgroup's 32 rows share their mask rows across its
+// heads, mask rows contiguous and 16-byte aligned): the 32 x 64 fp32 block of tile t, row-major
+// 256 bytes per row with the 16-byte chunks of row r stored at chunk ^ (r % 16), is copied
+// like K and V (8 blocks of 4 rows, split over the waves).  Rows past Tq and entries past the
+// mask's last valid entry read as zeros; other entries past Tk belong to keys that the select
+// removes.
+// ---------------------------------------------------------------------------------------
+template <int NW>
+struct MaskCopier {
+  static constexpr int MPW = 8 / NW;  // 1 KiB blocks each wave copies per tile
+  const unsigned char *base;          // mask row row0 of the workgroup, key 0
+  int64_t bytes_to_end;               // from base to the end of entry (Tq - 1, Tk - 1)
+  int wid;
+  uint32_t off[MPW];
+  __device__ __forceinline__ void init(const Params &p, int b, int row0, int wid_, int lane) {
+    wid = wid_;
+    base = reinterpret_cast<const unsigned char *>(p.mask + (int64_t)b * p.sm_b + (int64_t)row0 * p.sm_i);
+    bytes_to_end = ((int64_t)(p.Tq - 1 - row0) * p.sm_i + p.Tk) * 4;
+#pragma unroll
+    for (int i = 0; i < MPW; ++i) {
+      const int r = (wid * MPW + i) * 4 + lane / 16;
+      const uint32_t c = (uint32_t)(lane % 16) ^ (uint32_t)(r & 15);
+      off[i] = (uint32_t)(r * p.sm_i * 4) + c * 16u;
+    }
+  }
+  __device__ __forceinline__ BufRsrc rsrc(int t) const {
+    const int64_t skip = (int64_t)t * kBc * 4;
+    return make_rsrc(base + skip, bytes_to_end - skip);
+  }
+  __device__ __forceinline__ void copy(BufRsrc rs, int i, unsigned char *dst) const {
+    buf_load_lds16(rs, dst + (wid * MPW + i) * 1024, off[i]);
+  }
+};
+
+// ---------------------------------------------------------------------------------------
 // Streaming kernel (1, 2, 4 or 8 waves): each wave walks the tiles; the next tile is copied into
 // the other pair of LDS buffers while the current one is used, its copies spread over the QK
 // steps of the current tile.
@@ -878,6 +942,9 @@ fa_fwd_kernel(Params p0) {
   __shared__ __attribute__((aligned(1024))) unsigned char k1[L::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char v0[L::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char v1[L::TILE_BYTES];
+  constexpr int MBYTES = MODE == 1 ? 32 * 256 : 16;  // staged mask blocks (MODE 1)
+  __shared__ __attribute__((aligned(1024))) unsigned char m0[MBYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char m1[MBYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   Work wk(p0);
@@ -892,22 +959,36 @@ fa_fwd_kernel(Params p0) {
   wv.init(p, wk.b, head, wk.row0_blk + (wid / G) * kRowsWave, lane, wk.split == 0);
   CP cp;
   cp.init(p, wk.b, wk.kvh, wid, lane);
+  using MC = MaskCopier<NW>;
+  constexpr int NMC = MODE == 1 ? MC::MPW : 0;  // mask copies of a tile per wave
+  MC mc;
+  const bool mlds = MODE == 1 && p.mask_lds;
+  if (mlds) {
+    mc.init(p, wk.b, wk.row0_blk, wid, lane);
+    wv.mask_lds_row = (uint32_t)((wid / G) * kRowsWave + (lane & 31));
+  }
 
-  auto step = [&](int t, const unsigned char *kc, const unsigned char *vc, unsigned char *kn,
-                  unsigned char *vn) {
+  auto step = [&](int t, const unsigned char *kc, const unsigned char *vc, const unsigned char *mcur,
+                  unsigned char *kn, unsigned char *vn, unsigned char *mnext) {
     const bool has_next = t + 1 < wk.t_end;  // the buffers kn, vn were released by the last barrier
-    BufRsrc krs, vrs;
+    BufRsrc krs, vrs, mrs;
     cp.rsrcs(p, t + 1, krs, vrs);
+    if (mlds) mrs = mc.rsrc(t + 1);
     auto copies = [&](int ds) {  // copy i goes with QK step i * NDS / NCP
       if (has_next) {
 #pragma unroll
         for (int i = 0; i < NCP; ++i)
           if (i * NDS / NCP == ds) cp.copy(krs, vrs, i, kn, vn);
+        if (mlds) {
+#pragma unroll
+          for (int i = 0; i < NMC; ++i)
+            if (i * NDS / NMC == ds) mc.copy(mrs, i, mnext);
+        }
       }
     };
     if (wv.active(t)) {
       wv.template qk<true>(kc, wv.sacc, copies);
-      wv.softmax(p, t);
+      wv.softmax(p, t, mcur);
       wv.pv(vc);
     } else {
 #pragma unroll
@@ -918,12 +999,17 @@ fa_fwd_kernel(Params p0) {
   };
   if (wk.t_begin < wk.t_end) {
     cp.tiles(p, wk.t_begin, k0, v0);
+    if (mlds) {
+      const BufRsrc mrs = mc.rsrc(wk.t_begin);
+#pragma unroll
+      for (int i = 0; i < NMC; ++i) mc.copy(mrs, i, m0);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   for (int t = wk.t_begin; t < wk.t_end; t += 2) {
-    step(t, k0, v0, k1, v1);
-    if (t + 1 < wk.t_end) step(t + 1, k1, v1, k0, v0);
+    step(t, k0, v0, m0, k1, v1, m1);
+    if (t + 1 < wk.t_end) step(t + 1, k1, v1, m1, k0, v0, m0);
   }
   wv.finish(p, wk.b, head, wk.split);
 }
@@ -1242,6 +1328,7 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   p.n_blocks = (int32_t)n_blocks;
   p.causal = causal ? 1 : 0;
   p.scale_log2 = scale * kLog2e;
+  p.scale = scale;
   p.mask_vec = mask != nullptr && s.mask[3] == 1 && aligned(mask, 16) && s.mask[0] % 4 == 0 &&
                s.mask[1] % 4 == 0 && s.mask[2] % 4 == 0;
   p.tile_major = mask != nullptr && s.mask[0] == 0 && s.mask[1] == 0;
@@ -1267,6 +1354,9 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   // MODE 1 when scores need the explicit form: an additive mask, or a scale that is not
   // positive (the raw-maximum shortcut needs scale > 0).
   const int mode = (x.softcap > 0.f || x.alibi_slopes) ? 2 : (mask != nullptr || !(scale > 0.f)) ? 1 : 0;
+  // stage the mask through LDS when the workgroup's 32 rows share mask rows across its heads
+  p.mask_lds = mode == 1 && mask != nullptr && p.mask_vec && s.mask[1] == 0 && rows_pb == 32 &&
+               32 * s.mask[2] * 4 < INT32_MAX;
   KernelFn fn = bf16 ? (d == 64 ? pick_nw<true, 64>(nw, mode) : pick_nw<true, 128>(nw, mode))
                      : (d == 64 ? pick_nw<false, 64>(nw, mode) : pick_nw<false, 128>(nw, mode));
   (void)hipGetLastError();  // clear a stale error so the check below reports this launch
