@@ -946,7 +946,8 @@ fa_fwd_kernel(Params p0) {
   __shared__ __attribute__((aligned(1024))) unsigned char m0[MBYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char m1[MBYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // the wave index is uniform: keep it (and the LDS addresses derived from it) in SGPRs
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   Work wk(p0);
   const Params p = seq_params(p0, wk.b);
   wk.set_range(p);
