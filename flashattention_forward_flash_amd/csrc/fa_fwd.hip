@@ -48,6 +48,7 @@
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -221,9 +222,15 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 // the host pass (which never runs kernel bodies) sees stand-ins.
 #if defined(__HIP_DEVICE_COMPILE__)
 typedef __amdgpu_buffer_rsrc_t BufRsrc;
+// Every resource here is uniform over the wave; taking its words with readfirstlane keeps it
+// in SGPRs where the compiler cannot prove that (a resource in VGPRs costs a loop per load).
 __device__ __forceinline__ BufRsrc make_rsrc(const unsigned char *base, int64_t bytes) {
   const int64_t n = bytes < 0 ? 0 : (bytes < INT32_MAX ? bytes : INT32_MAX);
-  return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)n, 0x00020000 /* raw dwords */);
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const int nu = __builtin_amdgcn_readfirstlane((int)n);
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)(lo | (hi << 32)), (short)0, nu, 0x00020000 /* raw dwords */);
 }
 __device__ __forceinline__ void buf_load_lds16(BufRsrc rs, unsigned char *lds_block, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds_block, 16, off, 0, 0, 0);
@@ -273,6 +280,47 @@ __device__ __forceinline__ void lds_wait(T &a, T &b, T &c, T &d, T &e, T &f, T &
   asm volatile("s_waitcnt lgkmcnt(%8)"
                : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h)
                : "i"(N));
+}
+// The wait of the alternating schedule's matrix phase: the V^T and K operands of one step
+// (d 128: 8 + 4 registers, d 64: 4 + 2).
+template <int N, int NV, int NK>
+__device__ __forceinline__ void lds_wait_vk(s16x4 (&v)[NV], u32x4 (&k)[NK]) {
+  if constexpr (NV == 8 && NK == 4) {
+    asm volatile("s_waitcnt lgkmcnt(%12)"
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
+                   "+v"(v[7]), "+v"(k[0]), "+v"(k[1]), "+v"(k[2]), "+v"(k[3])
+                 : "i"(N));
+  } else {
+    static_assert(NV == 4 && NK == 2, "d 64 or 128");
+    asm volatile("s_waitcnt lgkmcnt(%6)"
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(k[0]), "+v"(k[1])
+                 : "i"(N));
+  }
+}
+// Waits until at most N of this wave's vector-memory operations (here: tile copies, which
+// complete in order) are outstanding.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
+// ds_write_b128 of `val` at LDS byte address `addr`, as inline assembly like the reads (ordered
+// with them and with the barriers); completion is waited for with lds_wait_all().
+__device__ __forceinline__ void lds_write_b128(uint32_t addr, const u32x4 &val) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(val));
+}
+__device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// A workgroup barrier that the compiler schedules nothing across: the phases of the
+// alternating schedule stay where they are written.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+// A uniform load of data that no kernel writes while this one runs (the block table), through
+// the scalar cache: it is counted by lgkmcnt, not by vmcnt, so it does not wait for the tile
+// copies in flight.
+__device__ __forceinline__ int32_t load_const(const int32_t *ptr) {
+  return *(const __attribute__((address_space(4))) int32_t *)ptr;
 }
 __device__ __forceinline__ uint32_t lds_addr(const unsigned char *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)p;
@@ -608,7 +656,9 @@ struct Wave {
 
   // Online-softmax step on the tile's scores: running maximum and denominator, and the weights
   // (the B operand of the PV MFMAs).  Returns alpha, the factor O^T must be multiplied by.
-  __device__ __forceinline__ float weights(const Params &p, const f32x16 (&sc)[2]) {
+  // `hook(0)` runs before the exponentials and `hook(1)` halfway through them.
+  template <typename Hook>
+  __device__ __forceinline__ float weights(const Params &p, const f32x16 (&sc)[2], Hook &&hook) {
     // row maximum (exact, so the reduction order is immaterial)
     float mx = sc[0][0];
 #pragma unroll
@@ -633,11 +683,13 @@ struct Wave {
     const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - shift);
 
     // weights and this half's partial denominator (fixed pairwise tree)
+    hook(0);
     float w[2][16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
+        if (kb == 1 && i == 0) hook(1);
         if constexpr (MODE == 0)
           w[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i], p.scale_log2, -shift));
         else if constexpr (MODE == 1)
@@ -645,15 +697,7 @@ struct Wave {
         else
           w[kb][i] = __builtin_amdgcn_exp2f(sc[kb][i] - shift);
       }
-    float s8[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      s8[j] = (w[j >> 2][4 * (j & 3)] + w[j >> 2][4 * (j & 3) + 1]) +
-              (w[j >> 2][4 * (j & 3) + 2] + w[j >> 2][4 * (j & 3) + 3]);
-    const float lsum = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
-    l_run = __builtin_fmaf(alpha, l_run, lsum);
-    m_run = m_new;
-
+    float lsum;
     if constexpr (BF16) {
       // MFMA c covers keys 16c..16c+15; lane half h supplies keys 16c + 8(j/4) + 4h + j%4,
       // which are its S^T registers i = 8(c%2) + j of block c/2.
@@ -661,12 +705,34 @@ struct Wave {
       for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int j = 0; j < 8; ++j) pb[c][j] = (__bf16)w[c >> 1][8 * (c & 1) + j];
+      // The denominator sums the weights as rounded for the PV product, so that o is a weighted
+      // mean of the values with weights summing to one (a row that sees one key gets that key's
+      // value exactly): pairs of bf16 weights by dot products with (1, 1), 16 keys per chain,
+      // the chains added in a fixed order.
+      const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x2 pr = {pb[c][2 * j], pb[c][2 * j + 1]};
+          acc[c] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc[c], false);
+        }
+      lsum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     } else {
+      float s8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        s8[j] = (w[j >> 2][4 * (j & 3)] + w[j >> 2][4 * (j & 3) + 1]) +
+                (w[j >> 2][4 * (j & 3) + 2] + w[j >> 2][4 * (j & 3) + 3]);
+      lsum = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) pw[kb][i] = w[kb][i];
     }
+    l_run = __builtin_fmaf(alpha, l_run, lsum);
+    m_run = m_new;
     return alpha;
   }
 
@@ -682,9 +748,13 @@ struct Wave {
 
   // The whole online-softmax step of tile t on `sacc`.
   __device__ __forceinline__ void softmax(const Params &p, int t, const unsigned char *ml = nullptr) {
+    softmax(p, t, ml, [](int) {});
+  }
+  template <typename Hook>
+  __device__ __forceinline__ void softmax(const Params &p, int t, const unsigned char *ml, Hook &&hook) {
     scores(p, t, sacc, ml);
     if (!full(t)) select(t, sacc);
-    rescale(weights(p, sacc));
+    rescale(weights(p, sacc, hook));
   }
 
   // O^T += V^T P^T with the tile's V in `vl`.  The MFMAs are ordered key block outer, d block
@@ -744,6 +814,69 @@ struct Wave {
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pw[kb][i], oacc[db], 0, 0, 0);
           }
         }
+    }
+  }
+  // The matrix phase of the alternating schedule (bf16): O^T += V^T P^T for the tile in `vl`
+  // (weights of the previous softmax in pb) and S^T = K Q^T for the next tile in `kl` into
+  // sacc, as 4 steps of one PV key block and D / 64 QK steps each.  The LDS operand reads of a
+  // step are issued one step ahead; `hook(c)` runs after those of step c + 1 are issued.
+  template <typename Hook>
+  __device__ __forceinline__ void pvqk(const unsigned char *vl, const unsigned char *kl, Hook &&hook) {
+    static_assert(BF16, "the alternating schedule is built for bf16");
+    constexpr int QPS = D / 64;  // QK steps (16 of d each) per step
+    // V^T operand addresses, as in pv()
+    const int r16 = lane & 15, dh = (lane >> 4) & 1;
+    const int key_l = 4 * half + (r16 >> 2);
+    const int d_l = 16 * dh + 4 * (r16 & 3);
+    const uint32_t vbase_l = lds_addr(vl) + key_l * (D * 2) + (d_l & 7) * 2;
+    uint32_t a0[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) a0[db] = vbase_l + ((((db * 32 + d_l) >> 3) ^ L::vsw(key_l)) * 16);
+    // K operand: row kb * 32 + lq, chunk (2 ds + half) swizzled by the row, as in qk()
+    const uint32_t krow = lds_addr(kl) + lq * (D * 2);
+    const int m = L::ksw(lq);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+    s16x4 vr[2][2 * NDB];   // [step parity][2 db + e]
+    u32x4 kr[2][2 * QPS];   // [step parity][2 j + kb]
+    auto issue = [&](int c) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        vr[c & 1][2 * db] = read_v(a0[db], c, 0);
+        vr[c & 1][2 * db + 1] = read_v(a0[db], c, 1);
+      }
+#pragma unroll
+      for (int j = 0; j < QPS; ++j) {
+        const uint32_t a = krow + ((((2 * (c * QPS + j) + half) ^ m)) << 4);
+        kr[c & 1][2 * j] = lds_read_b128<0>(a);
+        kr[c & 1][2 * j + 1] = lds_read_b128<32 * D * 2>(a);
+      }
+    };
+    issue(0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (c + 1 < 4) {
+        issue(c + 1);
+        hook(c);
+        lds_wait_vk<2 * NDB + 2 * QPS>(vr[c & 1], kr[c & 1]);
+      } else {
+        hook(c);
+        lds_wait_vk<0>(vr[c & 1], kr[c & 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < (NDB > 2 * QPS ? NDB : 2 * QPS); ++i) {
+        if (i < 2 * QPS) {
+          const int j = i >> 1, kb = i & 1;
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[c & 1][i]),
+                                                             qb[c * QPS + j], sacc[kb], 0, 0, 0);
+        }
+        if (i < NDB) {
+          const s16x8 both = __builtin_shufflevector(vr[c & 1][2 * i], vr[c & 1][2 * i + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb[c], oacc[i], 0, 0, 0);
+        }
+      }
     }
   }
   // transposing read of keys 16c + 8e + key_l (immediate offset), see pv()
@@ -827,6 +960,8 @@ struct Copier {
   const unsigned char *kbase, *vbase;  // the (b, KV head) slice, or the KV head in block 0 (paged)
   int64_t kbytes, vbytes;  // bytes of each slice from its first key to the end of key Tk - 1
   const int32_t *bt_row;   // paged: the block-table row of sequence b
+  BufRsrc kslice, vslice;  // contiguous: the slices, from their first key to the end of key Tk - 1
+  uint32_t kstep, vstep;   // contiguous: bytes from one tile of a slice to the next
   int wid;
   uint32_t koff[BPW], voff[BPW];
 
@@ -838,6 +973,10 @@ struct Copier {
     vbase = static_cast<const unsigned char *>(p.v) + (bk * p.sv_b + (int64_t)kvh * p.sv_h + p.k_start * p.sv_t) * ES;
     kbytes = ((int64_t)(p.Tk - 1) * p.sk_t + D) * ES;
     vbytes = ((int64_t)(p.Tk - 1) * p.sv_t + D) * ES;
+    kslice = make_rsrc(kbase, kbytes);
+    vslice = make_rsrc(vbase, vbytes);
+    kstep = (uint32_t)(kBc * p.sk_t * ES);
+    vstep = (uint32_t)(kBc * p.sv_t * ES);
     const int cp_row = lane / L::CH, cp_chunk = lane % L::CH;
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
@@ -852,13 +991,55 @@ struct Copier {
     const int64_t skip = (int64_t)t * kBc * (IS_K ? p.sk_t : p.sv_t) * ES;
     return make_rsrc((IS_K ? kbase : vbase) + skip, (IS_K ? kbytes : vbytes) - skip);
   }
+  // Resource of tile t of K (IS_K) or V.  Paged: the tile's rows in its block; rows past the
+  // sequence's keys, and a block index outside [0, num_blocks), read as zeros.
+  template <bool IS_K>
+  __device__ __forceinline__ BufRsrc tile_rsrc(const Params &p, int t) const {
+    const int64_t sb = IS_K ? p.sk_b : p.sv_b, st = IS_K ? p.sk_t : p.sv_t;
+    const unsigned char *ptr;
+    int64_t n;
+    if (bt_row) {
+      const uint32_t key0 = (uint32_t)t * kBc;  // < Tk < 2^31
+      const int64_t rows = min((int64_t)kBc, (int64_t)p.Tk - key0);
+      const int32_t blk = rows > 0 ? load_const(bt_row + key0 / (uint32_t)p.block_size) : -1;
+      const bool ok = blk >= 0 && blk < p.num_blocks;
+      const int64_t in_blk = key0 % (uint32_t)p.block_size;
+      ptr = (IS_K ? kbase : vbase) + ((ok ? blk : 0) * sb + in_blk * st) * ES;
+      n = ok ? ((rows - 1) * st + D) * ES : 0;
+    } else {
+      const int64_t skip = (int64_t)t * kBc * st * ES;
+      ptr = (IS_K ? kbase : vbase) + skip;
+      n = (IS_K ? kbytes : vbytes) - skip;
+    }
+    return make_rsrc(ptr, n);
+  }
+  // Where the copies of tile t of K (IS_K) or V read: a resource and a byte offset added to
+  // each lane's.  Contiguous: the slice and the tile's place in it (rows past Tk lie past the
+  // slice's end and read zeros; the host keeps a slice under 2 GiB, so the offsets of the
+  // tiles up to two past the last fit 32 bits); paged: the tile's own resource.
+  struct Src {
+    BufRsrc rs;
+    uint32_t add;
+  };
+  template <bool IS_K>
+  __device__ __forceinline__ Src src(const Params &p, int t) const {
+    if (bt_row) return Src{tile_rsrc<IS_K>(p, t), 0u};
+    return Src{IS_K ? kslice : vslice, (uint32_t)t * (IS_K ? kstep : vstep)};
+  }
+  // K copy i (of BPW) and V copy i of a tile from its sources.
+  __device__ __forceinline__ void copy_k(const Src &s, int i, unsigned char *kdst) const {
+    buf_load_lds16(s.rs, kdst + (wid * BPW + i) * 1024, koff[i] + s.add);
+  }
+  __device__ __forceinline__ void copy_v(const Src &s, int i, unsigned char *vdst) const {
+    buf_load_lds16(s.rs, vdst + (wid * BPW + i) * 1024, voff[i] + s.add);
+  }
   // Both resources of tile t.  Paged: the tile's rows in its block; rows past the sequence's
   // keys, and a block index outside [0, num_blocks), read as zeros.
   __device__ __forceinline__ void rsrcs(const Params &p, int t, BufRsrc &krs, BufRsrc &vrs) const {
     if (bt_row) {
       const uint32_t key0 = (uint32_t)t * kBc;  // < Tk < 2^31
       const int64_t rows = min((int64_t)kBc, (int64_t)p.Tk - key0);
-      const int32_t blk = rows > 0 ? bt_row[key0 / (uint32_t)p.block_size] : -1;
+      const int32_t blk = rows > 0 ? load_const(bt_row + key0 / (uint32_t)p.block_size) : -1;
       const bool ok = blk >= 0 && blk < p.num_blocks;
       const int64_t in_blk = key0 % (uint32_t)p.block_size;
       const int64_t bsel = ok ? blk : 0;
@@ -875,13 +1056,27 @@ struct Copier {
     if (i < BPW) buf_load_lds16(krs, kdst + (wid * BPW + i) * 1024, koff[i]);
     else buf_load_lds16(vrs, vdst + (wid * BPW + i - BPW) * 1024, voff[i - BPW]);
   }
+  // Register-staged form of copy i: get() loads this lane's 16 bytes of the block (the bytes
+  // that the buffer load to LDS would write at byte 16 lane of it) and put() writes them there.
+  __device__ __forceinline__ u32x4 get(BufRsrc krs, BufRsrc vrs, int i) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(i < BPW ? krs : vrs,
+                                                                          i < BPW ? koff[i] : voff[i - BPW], 0, 0));
+#else
+    return u32x4{};
+#endif
+  }
+  __device__ __forceinline__ void put(const u32x4 &val, int i, unsigned char *kdst, unsigned char *vdst,
+                                      int lane) const {
+    const unsigned char *blk = i < BPW ? kdst + (wid * BPW + i) * 1024 : vdst + (wid * BPW + i - BPW) * 1024;
+    lds_write_b128(lds_addr(blk) + 16u * (uint32_t)lane, val);
+  }
   __device__ __forceinline__ void tiles(const Params &p, int t, unsigned char *kdst, unsigned char *vdst) const {
-    BufRsrc krs, vrs;
-    rsrcs(p, t, krs, vrs);
+    const Src ks = src<true>(p, t), vs = src<false>(p, t);
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) buf_load_lds16(krs, kdst + (wid * BPW + i) * 1024, koff[i]);
+    for (int i = 0; i < BPW; ++i) copy_k(ks, i, kdst);
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) buf_load_lds16(vrs, vdst + (wid * BPW + i) * 1024, voff[i]);
+    for (int i = 0; i < BPW; ++i) copy_v(vs, i, vdst);
   }
 };
 
@@ -972,14 +1167,17 @@ fa_fwd_kernel(Params p0) {
   auto step = [&](int t, const unsigned char *kc, const unsigned char *vc, const unsigned char *mcur,
                   unsigned char *kn, unsigned char *vn, unsigned char *mnext) {
     const bool has_next = t + 1 < wk.t_end;  // the buffers kn, vn were released by the last barrier
-    BufRsrc krs, vrs, mrs;
-    cp.rsrcs(p, t + 1, krs, vrs);
+    const typename CP::Src ks = cp.template src<true>(p, t + 1), vs = cp.template src<false>(p, t + 1);
+    BufRsrc mrs;
     if (mlds) mrs = mc.rsrc(t + 1);
     auto copies = [&](int ds) {  // copy i goes with QK step i * NDS / NCP
       if (has_next) {
 #pragma unroll
         for (int i = 0; i < NCP; ++i)
-          if (i * NDS / NCP == ds) cp.copy(krs, vrs, i, kn, vn);
+          if (i * NDS / NCP == ds) {
+            if (i < CP::BPW) cp.copy_k(ks, i, kn);
+            else cp.copy_v(vs, i - CP::BPW, vn);
+          }
         if (mlds) {
 #pragma unroll
           for (int i = 0; i < NMC; ++i)
@@ -1011,6 +1209,131 @@ fa_fwd_kernel(Params p0) {
   for (int t = wk.t_begin; t < wk.t_end; t += 2) {
     step(t, k0, v0, m0, k1, v1, m1);
     if (t + 1 < wk.t_end) step(t + 1, k1, v1, m1, k0, v0, m0);
+  }
+  wv.finish(p, wk.b, head, wk.split);
+}
+
+// ---------------------------------------------------------------------------------------
+// Alternating kernel (bf16, no mask or score variant, 8 waves).  Waves w and w + 4 of a
+// workgroup share a SIMD.  Waves 0-3 and 4-7 run the per-tile work half a tile apart, so that
+// on every SIMD one wave's matrix phase (PV of tile t, then QK of tile t + 1, 32 MFMAs) meets
+// the other wave's softmax (vector ALU); a workgroup barrier separates the phases.  Per wave:
+//   QK(t0) | softmax(t0) | PV(t0) QK(t0 + 1) | softmax(t0 + 1) | ... | PV(t_end - 1)
+// with waves 4-7 one phase behind (one extra barrier at their start, and at the end of waves
+// 0-3, so every wave passes the same barriers).  Three K and three V tile buffers: the softmax
+// phase of tile t copies K(t + 2) into the buffer of K(t - 1) and the matrix phase copies
+// V(t + 2) into that of V(t - 1), which every wave has finished reading by then; each copy is
+// waited for by the end of the matrix phase before the one that reads it.  Every row's arithmetic
+// is that of fa_fwd_kernel (same tiles, same operations in the same order), so the two give
+// the same bits.
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+fa_fwd_pp_kernel(Params p0) {
+  using L = Layout<true, D>;
+  using CP = Copier<true, D, 8>;
+  constexpr int BPW = CP::BPW;       // copies per tensor per tile per wave
+  constexpr int NCP = 2 * BPW;       // copies of a matrix phase per wave
+  constexpr int NDS = D / 16;        // QK steps of a tile
+  constexpr int TB = L::TILE_BYTES;
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[3 * TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char vbuf[3 * TB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool late = wid >= 4;  // waves 4-7 run one phase behind
+  Work wk(p0);
+  const Params p = seq_params(p0, wk.b);
+  wk.set_range(p);
+  if (p.n_splits > 0 && wk.t_begin >= wk.t_end && (wk.split != 0 || p.sinks == nullptr)) return;
+  const int G = p.heads_per_block;
+  const int head = wk.head_base + wid % G;
+  Wave<true, D, 0> wv;
+  wv.init(p, wk.b, head, wk.row0_blk + (wid / G) * kRowsWave, lane, wk.split == 0);
+  CP cp;
+  cp.init(p, wk.b, wk.kvh, wid, lane);
+  const int t0 = wk.t_begin, t1 = wk.t_end;
+  if (t0 < t1) {
+    // tile t lives in buffer (t - t0) % 3 of kbuf and of vbuf
+    {
+      cp.tiles(p, t0, kbuf, vbuf);
+      if (t0 + 1 < t1) {
+        const typename CP::Src k1 = cp.template src<true>(p, t0 + 1);
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) cp.copy_k(k1, i, kbuf + TB);
+      }
+      vm_wait<0>();
+      phase_barrier();
+    }
+    if (late) phase_barrier();
+    // The copies after the first tiles, two per phase and wave, spread over the phase so that
+    // the workgroup's copies never queue up: the softmax phase of tile t copies K(t + 2) into
+    // K(t - 1)'s buffer, the matrix phase of tile t copies V(t + 2) into V(t - 1)'s; a wave
+    // waits for all but its newest copies at the end of each matrix phase.  Copies of tiles past
+    // the workgroup's last one still run (they read in-range data or zeros into a free buffer),
+    // which keeps the phases free of branches around them.
+    using Src = typename CP::Src;
+    auto copy_k = [&](const Src &ks, int ik, int i) {
+      __builtin_amdgcn_sched_barrier(0);
+      cp.copy_k(ks, i, kbuf + ik * TB);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto copy_v = [&](const Src &vs, int iv, int i) { cp.copy_v(vs, i, vbuf + iv * TB); };
+    // QK of the first tile, with the copies of V(t0 + 1)
+    {
+      __builtin_amdgcn_s_setprio(1);
+      const Src vrs = cp.template src<false>(p, t0 + 1);
+      if (wv.active(t0)) {
+        wv.template qk<true>(kbuf, wv.sacc, [&](int ds) {
+#pragma unroll
+          for (int i = 0; i < BPW; ++i)
+            if (ds == (2 * i + 1) * NDS / (2 * BPW)) copy_v(vrs, 1, i);
+        });
+      } else {
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) copy_v(vrs, 1, i);
+      }
+      __builtin_amdgcn_s_setprio(0);
+    }
+    phase_barrier();
+    int i0 = 0;  // buffer of tile t
+    for (int t = t0; t < t1; ++t) {
+      const int i1 = i0 == 2 ? 0 : i0 + 1, i2 = i1 == 2 ? 0 : i1 + 1;
+      // softmax phase, with the copies of K(t + 2)
+      {
+        const Src krs = cp.template src<true>(p, t + 2);
+        if (wv.active(t)) {
+          wv.softmax(p, t, nullptr, [&](int h) {
+#pragma unroll
+            for (int i = 0; i < BPW; ++i)
+              if (h == i * 2 / BPW) copy_k(krs, i2, i);
+          });
+        } else {
+#pragma unroll
+          for (int i = 0; i < BPW; ++i) copy_k(krs, i2, i);
+        }
+      }
+      phase_barrier();
+      // matrix phase: PV(t), QK(t + 1), with the copies of V(t + 2)
+      __builtin_amdgcn_s_setprio(1);
+      const Src vrs = cp.template src<false>(p, t + 2);
+      if (wv.active(t)) wv.pv(vbuf + i0 * TB);
+      __builtin_amdgcn_sched_barrier(0);  // PV's registers are free before QK's are taken
+      if (t + 1 < t1 && wv.active(t + 1)) {
+        wv.template qk<true>(kbuf + i1 * TB, wv.sacc, [&](int ds) {
+#pragma unroll
+          for (int i = 0; i < BPW; ++i)
+            if (ds == (2 * i + 1) * NDS / (2 * BPW)) copy_v(vrs, i2, i);
+        });
+      } else {
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) copy_v(vrs, i2, i);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      vm_wait<BPW>();
+      phase_barrier();
+      i0 = i1;
+    }
+    if (!late) phase_barrier();
   }
   wv.finish(p, wk.b, head, wk.split);
 }
@@ -1362,6 +1685,7 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
                32 * s.mask[2] * 4 < INT32_MAX;
   KernelFn fn = bf16 ? (d == 64 ? pick_nw<true, 64>(nw, mode) : pick_nw<true, 128>(nw, mode))
                      : (d == 64 ? pick_nw<false, 64>(nw, mode) : pick_nw<false, 128>(nw, mode));
+  if (bf16 && nw == 8 && mode == 0) fn = d == 64 ? fa_fwd_pp_kernel<64> : fa_fwd_pp_kernel<128>;
   (void)hipGetLastError();  // clear a stale error so the check below reports this launch
   hipLaunchKernelGGL(fn, dim3((unsigned)n_blocks), dim3(nw * 64), 0,
                      static_cast<hipStream_t>(stream), p);

@@ -1,0 +1,98 @@
+"""GPU tests of the alternating 8-wave kernel (bf16, no mask or score variant): two waves per
+SIMD run the matrix work of one tile while the other does the softmax of its own, with three
+K and three V tile buffers and the copies spread over both phases.
+
+Its rows must carry exactly the arithmetic of the 4-wave kernel ("FlashAttention forward in
+C", section 2.4: a row's result depends on its own data and position only), so every case is
+held bit for bit to the 4-wave tiling and to the fp64 oracle within the bf16 tolerance.  The
+cases cover the buffer rotation's edges: workgroups with 1, 2, 3 and 4 tiles (the prologue
+copies tiles t0 and t0 + 1; the first phases copy t0 + 2), rows whose visible tiles start late
+(q_offset, windows) or stop early (causal diagonal, ragged Tk), sinks, every 8-wave geometry,
+split-KV and paged keys.
+"""
+import numpy as np
+import pytest
+import torch
+
+import flashattention_forward_flash_amd as fa
+import oracle
+from gpu_common import bits, compare, dev, host, make_inputs, say, scale_for
+
+pytestmark = pytest.mark.gpu
+
+# (name, B, Hq, Hkv, Tq, Tk, d, q_offset, causal, window, sinks)
+CASES = [
+    ("one_tile", 1, 8, 2, 40, 50, 128, 0, True, 0, False),
+    ("two_tiles", 1, 8, 2, 64, 128, 128, 0, True, 0, True),
+    ("three_tiles_ragged", 2, 8, 2, 100, 150, 128, 50, True, 0, False),
+    ("four_tiles", 1, 4, 1, 64, 256, 128, 192, True, 0, False),
+    ("long_causal", 1, 8, 2, 700, 700, 128, 0, True, 0, True),
+    ("window", 1, 8, 2, 300, 1000, 128, 700, True, 130, False),
+    ("window_sinks_d64", 2, 8, 2, 257, 600, 64, 343, True, 65, True),
+    ("noncausal_ragged", 1, 8, 4, 77, 333, 128, 0, False, 0, False),
+    ("noncausal_d64", 1, 16, 2, 129, 1025, 64, 0, False, 0, True),
+    ("late_offset", 1, 8, 8, 33, 900, 128, 867, True, 0, False),
+]
+TILINGS = {1: [(256, 1)], 2: [(128, 2)], 4: [(64, 4)], 8: [(32, 8)]}
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_alternating_equals_four_wave(case):
+    name, B, Hq, Hkv, Tq, Tk, d, qo, causal, window, with_sinks = case
+    q, k, v, z = make_inputs(f"alt/{name}", B, Hq, Hkv, Tq, Tk, d, "bf16", sinks=with_sinks)
+    tq, tk, tv, tz = dev(q), dev(k), dev(v), dev(z)
+    kw = dict(scale=scale_for(d), q_offset=qo, causal=causal, window=window, sinks=tz)
+    group = Hq // Hkv
+    ref_tiling = (32, 4) if group % 4 == 0 else (32, 2) if group % 2 == 0 else (32, 1)
+    say("alternating", name, "reference tiling", ref_tiling)
+    o4, l4 = fa.forward(tq, tk, tv, tiling=ref_tiling, **kw)
+    torch.cuda.synchronize()
+    for til in TILINGS[group] + ([(64, 4)] if group == 8 else []) + ([(128, 2)] if group in (4, 8) else []):
+        say("alternating", name, "tiling", til)
+        o8, l8 = fa.forward(tq, tk, tv, tiling=til, **kw)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(o8), bits(o4)), f"O differs from the 4-wave kernel at tiling {til}"
+        assert np.array_equal(bits(l8), bits(l4)), f"LSE differs from the 4-wave kernel at tiling {til}"
+    o_ref, l_ref = oracle.attention(q, k, v, scale=kw["scale"], q_offset=qo, causal=causal, window=window, sinks=z)
+    compare(host(o4), host(l4), o_ref, l_ref, "bf16", f"alternating {name}")
+
+
+@pytest.mark.parametrize("split", [64, 192])
+def test_alternating_split_kv(split):
+    """Split-KV work items run through the alternating kernel when given an 8-wave tiling: the
+    same bits as through the 4-wave one."""
+    B, Hq, Hkv, Tq, Tk, d = 1, 8, 2, 130, 1000, 128
+    q, k, v, z = make_inputs(f"alt/split/{split}", B, Hq, Hkv, Tq, Tk, d, "bf16", sinks=True)
+    tq, tk, tv, tz = dev(q), dev(k), dev(v), dev(z)
+    kw = dict(scale=scale_for(d), q_offset=Tk - Tq, causal=True, sinks=tz, split_keys=split)
+    say("alternating split", split)
+    o4, l4 = fa.forward_splitkv(tq, tk, tv, tiling=(32, 4), **kw)
+    o8, l8 = fa.forward_splitkv(tq, tk, tv, tiling=(64, 4), **kw)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o8), bits(o4)) and np.array_equal(bits(l8), bits(l4))
+    o_ref, l_ref = oracle.attention(q, k, v, scale=kw["scale"], q_offset=Tk - Tq, causal=True, sinks=z)
+    compare(host(o8), host(l8), o_ref, l_ref, "bf16", f"alternating split {split}")
+
+
+def test_alternating_paged():
+    """Paged keys (block size 128, shuffled table) through the alternating kernel equal the
+    contiguous call bit for bit."""
+    from test_gpu_paged import _page
+    B, Hq, Hkv, Tq, Tk, d = 2, 8, 2, 200, 700, 128
+    q, k, v, _ = make_inputs("alt/paged", B, Hq, Hkv, Tq, Tk, d, "bf16")
+    tq, tk, tv = dev(q), dev(k), dev(v)
+    kp, vp, table = _page(tk, tv, 128, seed=4)
+    kw = dict(scale=scale_for(d), q_offset=Tk - Tq, causal=True, tiling=(64, 4))
+    say("alternating paged")
+    o1, l1 = fa.forward(tq, tk, tv, **kw)
+    o2, l2 = fa.forward_paged(tq, kp, vp, table, Tk=Tk, **kw)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o1), bits(o2)) and np.array_equal(bits(l1), bits(l2))
+
+
+def test_alternating_varlen():
+    """Packed sequences (lengths 0, 1 and around the tile edges) through the alternating kernel:
+    each sequence equals its own call bit for bit and the oracle within tolerance."""
+    from test_gpu_varlen import _check
+    lens = [1, 63, 64, 65, 300, 0, 129, 200]
+    _check(lens, lens, 8, 2, 128, "bf16", True, 0, True, 0, "alt/varlen", tiling=(64, 4))
