@@ -60,6 +60,7 @@ constexpr int kRowsWave = 32; // query rows per wave (N of the 32x32 MFMA)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.f;  // base-2 headroom before the running maximum is moved
+constexpr float kLazyW = 256.f;  // 2^kLazy
 #ifndef FA_QK_LOOKAHEAD
 #define FA_QK_LOOKAHEAD 2  // QK steps the K operand reads run ahead of the MFMAs
 #endif
@@ -281,41 +282,6 @@ __device__ __forceinline__ void lds_wait(T &a, T &b, T &c, T &d, T &e, T &f, T &
                : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h)
                : "i"(N));
 }
-// The wait of the alternating schedule's matrix phase: the V^T and K operands of one step
-// (d 128: 8 + 4 registers, d 64: 4 + 2).
-template <int N, int NV, int NK>
-__device__ __forceinline__ void lds_wait_vk(s16x4 (&v)[NV], u32x4 (&k)[NK]) {
-  if constexpr (NV == 8 && NK == 4) {
-    asm volatile("s_waitcnt lgkmcnt(%12)"
-                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
-                   "+v"(v[7]), "+v"(k[0]), "+v"(k[1]), "+v"(k[2]), "+v"(k[3])
-                 : "i"(N));
-  } else {
-    static_assert(NV == 4 && NK == 2, "d 64 or 128");
-    asm volatile("s_waitcnt lgkmcnt(%6)"
-                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(k[0]), "+v"(k[1])
-                 : "i"(N));
-  }
-}
-// Waits until at most N of this wave's vector-memory operations (here: tile copies, which
-// complete in order) are outstanding.
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
-}
-// ds_write_b128 of `val` at LDS byte address `addr`, as inline assembly like the reads (ordered
-// with them and with the barriers); completion is waited for with lds_wait_all().
-__device__ __forceinline__ void lds_write_b128(uint32_t addr, const u32x4 &val) {
-  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(val));
-}
-__device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-// A workgroup barrier that the compiler schedules nothing across: the phases of the
-// alternating schedule stay where they are written.
-__device__ __forceinline__ void phase_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-}
 // A uniform load of data that no kernel writes while this one runs (the block table), through
 // the scalar cache: it is counted by lgkmcnt, not by vmcnt, so it does not wait for the tile
 // copies in flight.
@@ -459,7 +425,7 @@ struct Wave {
         for (int e = 0; e < 4; ++e) qf[4 * c + e] = val[e];
       }
     }
-    m_run = -INFINITY;
+    m_run = row_ok ? -INFINITY : 0.f;  // rows past Tq are never written
     l_run = 0.f;
     if (p.sinks && with_sink) {  // a sink is the first "tile": m = z_h, l = e^0 = 1, a = 0
       m_run = p.sinks[head] * kLog2e;
@@ -654,42 +620,14 @@ struct Wave {
       }
   }
 
-  // Online-softmax step on the tile's scores: running maximum and denominator, and the weights
-  // (the B operand of the PV MFMAs).  Returns alpha, the factor O^T must be multiplied by.
-  // `hook(0)` runs before the exponentials and `hook(1)` halfway through them.
-  template <typename Hook>
-  __device__ __forceinline__ float weights(const Params &p, const f32x16 (&sc)[2], Hook &&hook) {
-    // row maximum (exact, so the reduction order is immaterial)
-    float mx = sc[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
-    // to base-2 units (a positive factor commutes with max and with fp32 rounding; -inf stays)
-    if constexpr (MODE == 0) mx = mx * p.scale_log2;
-    if constexpr (MODE == 1) mx = mx * kLog2e;
-    // The reference point m moves only when this tile's maximum exceeds it by more than
-    // kLazy (base-2 units), or m is still -inf: weights are then exp2(x - m) <= 2^kLazy, and
-    // most tiles need no rescale.  The rule depends on the row's own scores only, so a row's
-    // bits stay independent of chunking and query tiling.  The row maximum exceeds m + kLazy
-    // exactly when one lane half's maximum does, so the exchange between the halves is only
-    // needed when some lane's does.
-    float m_new = m_run;
-    if (__ballot(mx > m_run + kLazy)) {
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      m_new = (mx > m_run + kLazy) ? mx : m_run;
-    }
-    const float shift = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - shift);
-
-    // weights and this half's partial denominator (fixed pairwise tree)
-    hook(0);
+  // The tile's weights exp2(x - shift) in base-2 units (the B operand of the PV MFMAs) and this
+  // half's partial denominator.
+  __device__ __forceinline__ float expw(const Params &p, const f32x16 (&sc)[2], float shift) {
     float w[2][16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        if (kb == 1 && i == 0) hook(1);
         if constexpr (MODE == 0)
           w[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i], p.scale_log2, -shift));
         else if constexpr (MODE == 1)
@@ -731,6 +669,52 @@ struct Wave {
 #pragma unroll
         for (int i = 0; i < 16; ++i) pw[kb][i] = w[kb][i];
     }
+    return lsum;
+  }
+
+  // Online-softmax step on the tile's scores: reference point m, denominator l and the weights.
+  // Returns alpha, the factor O^T must be multiplied by.
+  //
+  // The reference point moves only when the tile's row maximum exceeds it by more than kLazy
+  // (base-2 units), or m is still -inf: weights are then exp2(x - m) <= 2^kLazy, and most
+  // tiles need no rescale.  The rule depends on the row's own scores only, so a row's bits stay
+  // independent of chunking and query tiling.
+  //
+  // MODE 0 and 1 first compute the weights against the current m.  When every lane's partial
+  // denominator stays below 2^kLazy and no m is -inf, every weight is below 2^kLazy, so every
+  // x - m is below kLazy (exp2 and the bf16 rounding are monotonic and exact at 2^kLazy) and
+  // the rule keeps m: those weights are the tile's, and the row maximum is never taken.
+  // Otherwise the maximum decides as stated, and the weights are recomputed for the rows whose
+  // m moved.  Both ways give the same bits.  MODE 2 takes the maximum first: under ALiBi the
+  // reference point of many rows moves at every tile.
+  __device__ __forceinline__ float weights(const Params &p, const f32x16 (&sc)[2]) {
+    float lsum = 0.f;
+    if constexpr (MODE != 2) {
+      lsum = expw(p, sc, m_run == -INFINITY ? 0.f : m_run);
+      if (!__ballot(m_run == -INFINITY || !(lsum < kLazyW))) {
+        l_run = __builtin_fmaf(1.f, l_run, lsum);
+        return 1.f;
+      }
+    }
+    // row maximum (exact, so the reduction order is immaterial)
+    float mx = sc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
+    // to base-2 units (a positive factor commutes with max and with fp32 rounding; -inf stays)
+    if constexpr (MODE == 0) mx = mx * p.scale_log2;
+    if constexpr (MODE == 1) mx = mx * kLog2e;
+    // The row maximum exceeds m + kLazy exactly when one lane half's maximum does, so the
+    // exchange between the halves is only needed when some lane's does.
+    float m_new = m_run;
+    if (__ballot(mx > m_run + kLazy)) {
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      m_new = (mx > m_run + kLazy) ? mx : m_run;
+    }
+    const float shift = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - shift);
+    if (MODE == 2 || __ballot(m_new != m_run)) lsum = expw(p, sc, shift);
     l_run = __builtin_fmaf(alpha, l_run, lsum);
     m_run = m_new;
     return alpha;
@@ -748,13 +732,9 @@ struct Wave {
 
   // The whole online-softmax step of tile t on `sacc`.
   __device__ __forceinline__ void softmax(const Params &p, int t, const unsigned char *ml = nullptr) {
-    softmax(p, t, ml, [](int) {});
-  }
-  template <typename Hook>
-  __device__ __forceinline__ void softmax(const Params &p, int t, const unsigned char *ml, Hook &&hook) {
     scores(p, t, sacc, ml);
     if (!full(t)) select(t, sacc);
-    rescale(weights(p, sacc, hook));
+    rescale(weights(p, sacc));
   }
 
   // O^T += V^T P^T with the tile's V in `vl`.  The MFMAs are ordered key block outer, d block
@@ -814,69 +794,6 @@ struct Wave {
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pw[kb][i], oacc[db], 0, 0, 0);
           }
         }
-    }
-  }
-  // The matrix phase of the alternating schedule (bf16): O^T += V^T P^T for the tile in `vl`
-  // (weights of the previous softmax in pb) and S^T = K Q^T for the next tile in `kl` into
-  // sacc, as 4 steps of one PV key block and D / 64 QK steps each.  The LDS operand reads of a
-  // step are issued one step ahead; `hook(c)` runs after those of step c + 1 are issued.
-  template <typename Hook>
-  __device__ __forceinline__ void pvqk(const unsigned char *vl, const unsigned char *kl, Hook &&hook) {
-    static_assert(BF16, "the alternating schedule is built for bf16");
-    constexpr int QPS = D / 64;  // QK steps (16 of d each) per step
-    // V^T operand addresses, as in pv()
-    const int r16 = lane & 15, dh = (lane >> 4) & 1;
-    const int key_l = 4 * half + (r16 >> 2);
-    const int d_l = 16 * dh + 4 * (r16 & 3);
-    const uint32_t vbase_l = lds_addr(vl) + key_l * (D * 2) + (d_l & 7) * 2;
-    uint32_t a0[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) a0[db] = vbase_l + ((((db * 32 + d_l) >> 3) ^ L::vsw(key_l)) * 16);
-    // K operand: row kb * 32 + lq, chunk (2 ds + half) swizzled by the row, as in qk()
-    const uint32_t krow = lds_addr(kl) + lq * (D * 2);
-    const int m = L::ksw(lq);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-    s16x4 vr[2][2 * NDB];   // [step parity][2 db + e]
-    u32x4 kr[2][2 * QPS];   // [step parity][2 j + kb]
-    auto issue = [&](int c) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        vr[c & 1][2 * db] = read_v(a0[db], c, 0);
-        vr[c & 1][2 * db + 1] = read_v(a0[db], c, 1);
-      }
-#pragma unroll
-      for (int j = 0; j < QPS; ++j) {
-        const uint32_t a = krow + ((((2 * (c * QPS + j) + half) ^ m)) << 4);
-        kr[c & 1][2 * j] = lds_read_b128<0>(a);
-        kr[c & 1][2 * j + 1] = lds_read_b128<32 * D * 2>(a);
-      }
-    };
-    issue(0);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (c + 1 < 4) {
-        issue(c + 1);
-        hook(c);
-        lds_wait_vk<2 * NDB + 2 * QPS>(vr[c & 1], kr[c & 1]);
-      } else {
-        hook(c);
-        lds_wait_vk<0>(vr[c & 1], kr[c & 1]);
-      }
-#pragma unroll
-      for (int i = 0; i < (NDB > 2 * QPS ? NDB : 2 * QPS); ++i) {
-        if (i < 2 * QPS) {
-          const int j = i >> 1, kb = i & 1;
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[c & 1][i]),
-                                                             qb[c * QPS + j], sacc[kb], 0, 0, 0);
-        }
-        if (i < NDB) {
-          const s16x8 both = __builtin_shufflevector(vr[c & 1][2 * i], vr[c & 1][2 * i + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb[c], oacc[i], 0, 0, 0);
-        }
-      }
     }
   }
   // transposing read of keys 16c + 8e + key_l (immediate offset), see pv()
@@ -985,45 +902,30 @@ struct Copier {
       voff[i] = (uint32_t)(r * p.sv_t * ES) + ((cp_chunk ^ L::vsw(r)) * 16);
     }
   }
-  // Buffer resource of tile t of K (IS_K) or V: the tile and the rest of the slice.
+  // Paged: the resource of tile t of K (IS_K) or V, the tile's rows in its block; rows past
+  // the sequence's keys, and a block index outside [0, num_blocks), read as zeros.
   template <bool IS_K>
-  __device__ __forceinline__ BufRsrc rsrc(const Params &p, int t) const {
-    const int64_t skip = (int64_t)t * kBc * (IS_K ? p.sk_t : p.sv_t) * ES;
-    return make_rsrc((IS_K ? kbase : vbase) + skip, (IS_K ? kbytes : vbytes) - skip);
-  }
-  // Resource of tile t of K (IS_K) or V.  Paged: the tile's rows in its block; rows past the
-  // sequence's keys, and a block index outside [0, num_blocks), read as zeros.
-  template <bool IS_K>
-  __device__ __forceinline__ BufRsrc tile_rsrc(const Params &p, int t) const {
+  __device__ __forceinline__ BufRsrc paged_rsrc(const Params &p, int t) const {
     const int64_t sb = IS_K ? p.sk_b : p.sv_b, st = IS_K ? p.sk_t : p.sv_t;
-    const unsigned char *ptr;
-    int64_t n;
-    if (bt_row) {
-      const uint32_t key0 = (uint32_t)t * kBc;  // < Tk < 2^31
-      const int64_t rows = min((int64_t)kBc, (int64_t)p.Tk - key0);
-      const int32_t blk = rows > 0 ? load_const(bt_row + key0 / (uint32_t)p.block_size) : -1;
-      const bool ok = blk >= 0 && blk < p.num_blocks;
-      const int64_t in_blk = key0 % (uint32_t)p.block_size;
-      ptr = (IS_K ? kbase : vbase) + ((ok ? blk : 0) * sb + in_blk * st) * ES;
-      n = ok ? ((rows - 1) * st + D) * ES : 0;
-    } else {
-      const int64_t skip = (int64_t)t * kBc * st * ES;
-      ptr = (IS_K ? kbase : vbase) + skip;
-      n = (IS_K ? kbytes : vbytes) - skip;
-    }
-    return make_rsrc(ptr, n);
+    const uint32_t key0 = (uint32_t)t * kBc;  // < Tk < 2^31
+    const int64_t rows = min((int64_t)kBc, (int64_t)p.Tk - key0);
+    const int32_t blk = rows > 0 ? load_const(bt_row + key0 / (uint32_t)p.block_size) : -1;
+    const bool ok = blk >= 0 && blk < p.num_blocks;
+    const int64_t in_blk = key0 % (uint32_t)p.block_size;
+    return make_rsrc((IS_K ? kbase : vbase) + ((ok ? blk : 0) * sb + in_blk * st) * ES,
+                     ok ? ((rows - 1) * st + D) * ES : 0);
   }
   // Where the copies of tile t of K (IS_K) or V read: a resource and a byte offset added to
   // each lane's.  Contiguous: the slice and the tile's place in it (rows past Tk lie past the
-  // slice's end and read zeros; the host keeps a slice under 2 GiB, so the offsets of the
-  // tiles up to two past the last fit 32 bits); paged: the tile's own resource.
+  // slice's end and read zeros; the host keeps a slice under 2 GiB, so the offsets fit 32
+  // bits); paged: the tile's own resource.
   struct Src {
     BufRsrc rs;
     uint32_t add;
   };
   template <bool IS_K>
   __device__ __forceinline__ Src src(const Params &p, int t) const {
-    if (bt_row) return Src{tile_rsrc<IS_K>(p, t), 0u};
+    if (bt_row) return Src{paged_rsrc<IS_K>(p, t), 0u};
     return Src{IS_K ? kslice : vslice, (uint32_t)t * (IS_K ? kstep : vstep)};
   }
   // K copy i (of BPW) and V copy i of a tile from its sources.
@@ -1032,44 +934,6 @@ struct Copier {
   }
   __device__ __forceinline__ void copy_v(const Src &s, int i, unsigned char *vdst) const {
     buf_load_lds16(s.rs, vdst + (wid * BPW + i) * 1024, voff[i] + s.add);
-  }
-  // Both resources of tile t.  Paged: the tile's rows in its block; rows past the sequence's
-  // keys, and a block index outside [0, num_blocks), read as zeros.
-  __device__ __forceinline__ void rsrcs(const Params &p, int t, BufRsrc &krs, BufRsrc &vrs) const {
-    if (bt_row) {
-      const uint32_t key0 = (uint32_t)t * kBc;  // < Tk < 2^31
-      const int64_t rows = min((int64_t)kBc, (int64_t)p.Tk - key0);
-      const int32_t blk = rows > 0 ? load_const(bt_row + key0 / (uint32_t)p.block_size) : -1;
-      const bool ok = blk >= 0 && blk < p.num_blocks;
-      const int64_t in_blk = key0 % (uint32_t)p.block_size;
-      const int64_t bsel = ok ? blk : 0;
-      krs = make_rsrc(kbase + (bsel * p.sk_b + in_blk * p.sk_t) * ES, ok ? ((rows - 1) * p.sk_t + D) * ES : 0);
-      vrs = make_rsrc(vbase + (bsel * p.sv_b + in_blk * p.sv_t) * ES, ok ? ((rows - 1) * p.sv_t + D) * ES : 0);
-    } else {
-      krs = rsrc<true>(p, t);
-      vrs = rsrc<false>(p, t);
-    }
-  }
-  // Copy i of this wave's 2 * BPW copies of a tile: K blocks first, then V blocks.
-  __device__ __forceinline__ void copy(BufRsrc krs, BufRsrc vrs, int i, unsigned char *kdst,
-                                       unsigned char *vdst) const {
-    if (i < BPW) buf_load_lds16(krs, kdst + (wid * BPW + i) * 1024, koff[i]);
-    else buf_load_lds16(vrs, vdst + (wid * BPW + i - BPW) * 1024, voff[i - BPW]);
-  }
-  // Register-staged form of copy i: get() loads this lane's 16 bytes of the block (the bytes
-  // that the buffer load to LDS would write at byte 16 lane of it) and put() writes them there.
-  __device__ __forceinline__ u32x4 get(BufRsrc krs, BufRsrc vrs, int i) const {
-#if defined(__HIP_DEVICE_COMPILE__)
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(i < BPW ? krs : vrs,
-                                                                          i < BPW ? koff[i] : voff[i - BPW], 0, 0));
-#else
-    return u32x4{};
-#endif
-  }
-  __device__ __forceinline__ void put(const u32x4 &val, int i, unsigned char *kdst, unsigned char *vdst,
-                                      int lane) const {
-    const unsigned char *blk = i < BPW ? kdst + (wid * BPW + i) * 1024 : vdst + (wid * BPW + i - BPW) * 1024;
-    lds_write_b128(lds_addr(blk) + 16u * (uint32_t)lane, val);
   }
   __device__ __forceinline__ void tiles(const Params &p, int t, unsigned char *kdst, unsigned char *vdst) const {
     const Src ks = src<true>(p, t), vs = src<false>(p, t);
@@ -1214,131 +1078,6 @@ fa_fwd_kernel(Params p0) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Alternating kernel (bf16, no mask or score variant, 8 waves).  Waves w and w + 4 of a
-// workgroup share a SIMD.  Waves 0-3 and 4-7 run the per-tile work half a tile apart, so that
-// on every SIMD one wave's matrix phase (PV of tile t, then QK of tile t + 1, 32 MFMAs) meets
-// the other wave's softmax (vector ALU); a workgroup barrier separates the phases.  Per wave:
-//   QK(t0) | softmax(t0) | PV(t0) QK(t0 + 1) | softmax(t0 + 1) | ... | PV(t_end - 1)
-// with waves 4-7 one phase behind (one extra barrier at their start, and at the end of waves
-// 0-3, so every wave passes the same barriers).  Three K and three V tile buffers: the softmax
-// phase of tile t copies K(t + 2) into the buffer of K(t - 1) and the matrix phase copies
-// V(t + 2) into that of V(t - 1), which every wave has finished reading by then; each copy is
-// waited for by the end of the matrix phase before the one that reads it.  Every row's arithmetic
-// is that of fa_fwd_kernel (same tiles, same operations in the same order), so the two give
-// the same bits.
-// ---------------------------------------------------------------------------------------
-template <int D>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
-fa_fwd_pp_kernel(Params p0) {
-  using L = Layout<true, D>;
-  using CP = Copier<true, D, 8>;
-  constexpr int BPW = CP::BPW;       // copies per tensor per tile per wave
-  constexpr int NCP = 2 * BPW;       // copies of a matrix phase per wave
-  constexpr int NDS = D / 16;        // QK steps of a tile
-  constexpr int TB = L::TILE_BYTES;
-  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[3 * TB];
-  __shared__ __attribute__((aligned(1024))) unsigned char vbuf[3 * TB];
-
-  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool late = wid >= 4;  // waves 4-7 run one phase behind
-  Work wk(p0);
-  const Params p = seq_params(p0, wk.b);
-  wk.set_range(p);
-  if (p.n_splits > 0 && wk.t_begin >= wk.t_end && (wk.split != 0 || p.sinks == nullptr)) return;
-  const int G = p.heads_per_block;
-  const int head = wk.head_base + wid % G;
-  Wave<true, D, 0> wv;
-  wv.init(p, wk.b, head, wk.row0_blk + (wid / G) * kRowsWave, lane, wk.split == 0);
-  CP cp;
-  cp.init(p, wk.b, wk.kvh, wid, lane);
-  const int t0 = wk.t_begin, t1 = wk.t_end;
-  if (t0 < t1) {
-    // tile t lives in buffer (t - t0) % 3 of kbuf and of vbuf
-    {
-      cp.tiles(p, t0, kbuf, vbuf);
-      if (t0 + 1 < t1) {
-        const typename CP::Src k1 = cp.template src<true>(p, t0 + 1);
-#pragma unroll
-        for (int i = 0; i < BPW; ++i) cp.copy_k(k1, i, kbuf + TB);
-      }
-      vm_wait<0>();
-      phase_barrier();
-    }
-    if (late) phase_barrier();
-    // The copies after the first tiles, two per phase and wave, spread over the phase so that
-    // the workgroup's copies never queue up: the softmax phase of tile t copies K(t + 2) into
-    // K(t - 1)'s buffer, the matrix phase of tile t copies V(t + 2) into V(t - 1)'s; a wave
-    // waits for all but its newest copies at the end of each matrix phase.  Copies of tiles past
-    // the workgroup's last one still run (they read in-range data or zeros into a free buffer),
-    // which keeps the phases free of branches around them.
-    using Src = typename CP::Src;
-    auto copy_k = [&](const Src &ks, int ik, int i) {
-      __builtin_amdgcn_sched_barrier(0);
-      cp.copy_k(ks, i, kbuf + ik * TB);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    auto copy_v = [&](const Src &vs, int iv, int i) { cp.copy_v(vs, i, vbuf + iv * TB); };
-    // QK of the first tile, with the copies of V(t0 + 1)
-    {
-      __builtin_amdgcn_s_setprio(1);
-      const Src vrs = cp.template src<false>(p, t0 + 1);
-      if (wv.active(t0)) {
-        wv.template qk<true>(kbuf, wv.sacc, [&](int ds) {
-#pragma unroll
-          for (int i = 0; i < BPW; ++i)
-            if (ds == (2 * i + 1) * NDS / (2 * BPW)) copy_v(vrs, 1, i);
-        });
-      } else {
-#pragma unroll
-        for (int i = 0; i < BPW; ++i) copy_v(vrs, 1, i);
-      }
-      __builtin_amdgcn_s_setprio(0);
-    }
-    phase_barrier();
-    int i0 = 0;  // buffer of tile t
-    for (int t = t0; t < t1; ++t) {
-      const int i1 = i0 == 2 ? 0 : i0 + 1, i2 = i1 == 2 ? 0 : i1 + 1;
-      // softmax phase, with the copies of K(t + 2)
-      {
-        const Src krs = cp.template src<true>(p, t + 2);
-        if (wv.active(t)) {
-          wv.softmax(p, t, nullptr, [&](int h) {
-#pragma unroll
-            for (int i = 0; i < BPW; ++i)
-              if (h == i * 2 / BPW) copy_k(krs, i2, i);
-          });
-        } else {
-#pragma unroll
-          for (int i = 0; i < BPW; ++i) copy_k(krs, i2, i);
-        }
-      }
-      phase_barrier();
-      // matrix phase: PV(t), QK(t + 1), with the copies of V(t + 2)
-      __builtin_amdgcn_s_setprio(1);
-      const Src vrs = cp.template src<false>(p, t + 2);
-      if (wv.active(t)) wv.pv(vbuf + i0 * TB);
-      __builtin_amdgcn_sched_barrier(0);  // PV's registers are free before QK's are taken
-      if (t + 1 < t1 && wv.active(t + 1)) {
-        wv.template qk<true>(kbuf + i1 * TB, wv.sacc, [&](int ds) {
-#pragma unroll
-          for (int i = 0; i < BPW; ++i)
-            if (ds == (2 * i + 1) * NDS / (2 * BPW)) copy_v(vrs, i2, i);
-        });
-      } else {
-#pragma unroll
-        for (int i = 0; i < BPW; ++i) copy_v(vrs, i2, i);
-      }
-      __builtin_amdgcn_s_setprio(0);
-      vm_wait<BPW>();
-      phase_barrier();
-      i0 = i1;
-    }
-    if (!late) phase_barrier();
-  }
-  wv.finish(p, wk.b, head, wk.split);
-}
-
-// ---------------------------------------------------------------------------------------
 // Split-KV merge ("FlashAttention forward in C", "Going further": the partial (m, l, a) of
 // the key splits are combined with the same rescale as the tiles).  One wave per query row
 // that sees more than one split, over the splits that meet the row's visible keys (and split 0
@@ -1466,12 +1205,12 @@ KernelFn pick_nw(int nw, int mode) {
 
 bool aligned(const void *ptr, int64_t a) { return (reinterpret_cast<uintptr_t>(ptr) % (uintptr_t)a) == 0; }
 
-// Picks (rows_per_block, heads_per_block): prefer 4 waves (8 for the bf16 kernels without a
-// mask or score variant, measured 2-4 % faster there) with as many heads of one KV group as
-// divide the group, and fall back to fewer waves per workgroup when that leaves the 256 CUs
-// with too few workgroups.  Any choice gives the same bits.
-void auto_tiling(int64_t B, int64_t Hkv, int64_t group, int64_t Tq, bool wide, int32_t *rows, int32_t *heads) {
-  for (int nw = wide ? 8 : 4; nw >= 1; nw /= 2) {
+// Picks (rows_per_block, heads_per_block): prefer 4 waves (8 measure the same or up to 1 %
+// slower) with as many heads of one KV group as divide the group, and fall back to fewer waves
+// per workgroup when that leaves the 256 CUs with too few workgroups.  Any choice gives the
+// same bits.
+void auto_tiling(int64_t B, int64_t Hkv, int64_t group, int64_t Tq, int32_t *rows, int32_t *heads) {
+  for (int nw = 4; nw >= 1; nw /= 2) {
     int g = 1;
     for (int c = nw; c >= 2; c /= 2)
       if (group % c == 0) { g = c; break; }
@@ -1624,9 +1363,8 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
       (((Tk - 1) * s.k[2] + d) * es >= INT32_MAX || ((Tk - 1) * s.v[2] + d) * es >= INT32_MAX))
     return FA_EUNSUPPORTED;
   if (rows_pb == 0) {
-    const bool mode0 = mask == nullptr && scale > 0.f && !(x.softcap > 0.f) && x.alibi_slopes == nullptr;
     if (split) split_tiling(group, Tq, &rows_pb, &heads_pb);
-    else auto_tiling(B, Hkv, group, Tq, dtype == FA_BF16 && mode0, &rows_pb, &heads_pb);
+    else auto_tiling(B, Hkv, group, Tq, &rows_pb, &heads_pb);
   }
   const int nw = (int)((int64_t)rows_pb * heads_pb / 32);
   const int64_t n_row_tiles = (Tq + rows_pb - 1) / rows_pb;
@@ -1685,7 +1423,6 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
                32 * s.mask[2] * 4 < INT32_MAX;
   KernelFn fn = bf16 ? (d == 64 ? pick_nw<true, 64>(nw, mode) : pick_nw<true, 128>(nw, mode))
                      : (d == 64 ? pick_nw<false, 64>(nw, mode) : pick_nw<false, 128>(nw, mode));
-  if (bf16 && nw == 8 && mode == 0) fn = d == 64 ? fa_fwd_pp_kernel<64> : fa_fwd_pp_kernel<128>;
   (void)hipGetLastError();  // clear a stale error so the check below reports this launch
   hipLaunchKernelGGL(fn, dim3((unsigned)n_blocks), dim3(nw * 64), 0,
                      static_cast<hipStream_t>(stream), p);

@@ -1,14 +1,11 @@
-"""GPU tests of the alternating 8-wave kernel (bf16, no mask or score variant): two waves per
-SIMD run the matrix work of one tile while the other does the softmax of its own, with three
-K and three V tile buffers and the copies spread over both phases.
+"""GPU tests of the 8-wave geometries (two waves per SIMD, 64 to 256 rows of one to four heads
+per workgroup, with 32 KiB of K/V tiles staged for eight waves) against the 4-wave kernel.
 
-Its rows must carry exactly the arithmetic of the 4-wave kernel ("FlashAttention forward in
-C", section 2.4: a row's result depends on its own data and position only), so every case is
-held bit for bit to the 4-wave tiling and to the fp64 oracle within the bf16 tolerance.  The
-cases cover the buffer rotation's edges: workgroups with 1, 2, 3 and 4 tiles (the prologue
-copies tiles t0 and t0 + 1; the first phases copy t0 + 2), rows whose visible tiles start late
-(q_offset, windows) or stop early (causal diagonal, ragged Tk), sinks, every 8-wave geometry,
-split-KV and paged keys.
+A row's result depends on its own data and position only ("FlashAttention forward in C",
+section 2.4), so every case is held bit for bit to the 4-wave tiling and to the fp64 oracle
+within the bf16 tolerance.  The cases cover workgroups with 1, 2, 3 and 4 tiles and longer,
+rows whose visible tiles start late (q_offset, windows) or stop early (causal diagonal, ragged
+Tk), sinks, d 64, split-KV, paged keys and packed sequences.
 """
 import numpy as np
 import pytest
@@ -37,62 +34,84 @@ TILINGS = {1: [(256, 1)], 2: [(128, 2)], 4: [(64, 4)], 8: [(32, 8)]}
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_alternating_equals_four_wave(case):
+def test_eight_waves_equal_four(case):
     name, B, Hq, Hkv, Tq, Tk, d, qo, causal, window, with_sinks = case
     q, k, v, z = make_inputs(f"alt/{name}", B, Hq, Hkv, Tq, Tk, d, "bf16", sinks=with_sinks)
     tq, tk, tv, tz = dev(q), dev(k), dev(v), dev(z)
     kw = dict(scale=scale_for(d), q_offset=qo, causal=causal, window=window, sinks=tz)
     group = Hq // Hkv
     ref_tiling = (32, 4) if group % 4 == 0 else (32, 2) if group % 2 == 0 else (32, 1)
-    say("alternating", name, "reference tiling", ref_tiling)
+    say("8-wave", name, "reference tiling", ref_tiling)
     o4, l4 = fa.forward(tq, tk, tv, tiling=ref_tiling, **kw)
     torch.cuda.synchronize()
     for til in TILINGS[group] + ([(64, 4)] if group == 8 else []) + ([(128, 2)] if group in (4, 8) else []):
-        say("alternating", name, "tiling", til)
+        say("8-wave", name, "tiling", til)
         o8, l8 = fa.forward(tq, tk, tv, tiling=til, **kw)
         torch.cuda.synchronize()
         assert np.array_equal(bits(o8), bits(o4)), f"O differs from the 4-wave kernel at tiling {til}"
         assert np.array_equal(bits(l8), bits(l4)), f"LSE differs from the 4-wave kernel at tiling {til}"
     o_ref, l_ref = oracle.attention(q, k, v, scale=kw["scale"], q_offset=qo, causal=causal, window=window, sinks=z)
-    compare(host(o4), host(l4), o_ref, l_ref, "bf16", f"alternating {name}")
+    compare(host(o4), host(l4), o_ref, l_ref, "bf16", f"8-wave {name}")
 
 
 @pytest.mark.parametrize("split", [64, 192])
-def test_alternating_split_kv(split):
-    """Split-KV work items run through the alternating kernel when given an 8-wave tiling: the
-    same bits as through the 4-wave one."""
+def test_eight_waves_split_kv(split):
+    """Split-KV work items with an 8-wave tiling: the same bits as with the 4-wave one."""
     B, Hq, Hkv, Tq, Tk, d = 1, 8, 2, 130, 1000, 128
     q, k, v, z = make_inputs(f"alt/split/{split}", B, Hq, Hkv, Tq, Tk, d, "bf16", sinks=True)
     tq, tk, tv, tz = dev(q), dev(k), dev(v), dev(z)
     kw = dict(scale=scale_for(d), q_offset=Tk - Tq, causal=True, sinks=tz, split_keys=split)
-    say("alternating split", split)
+    say("8-wave split", split)
     o4, l4 = fa.forward_splitkv(tq, tk, tv, tiling=(32, 4), **kw)
     o8, l8 = fa.forward_splitkv(tq, tk, tv, tiling=(64, 4), **kw)
     torch.cuda.synchronize()
     assert np.array_equal(bits(o8), bits(o4)) and np.array_equal(bits(l8), bits(l4))
     o_ref, l_ref = oracle.attention(q, k, v, scale=kw["scale"], q_offset=Tk - Tq, causal=True, sinks=z)
-    compare(host(o8), host(l8), o_ref, l_ref, "bf16", f"alternating split {split}")
+    compare(host(o8), host(l8), o_ref, l_ref, "bf16", f"8-wave split {split}")
 
 
-def test_alternating_paged():
-    """Paged keys (block size 128, shuffled table) through the alternating kernel equal the
-    contiguous call bit for bit."""
+def test_eight_waves_paged():
+    """Paged keys (block size 128, shuffled table) with an 8-wave tiling equal the contiguous
+    call bit for bit."""
     from test_gpu_paged import _page
     B, Hq, Hkv, Tq, Tk, d = 2, 8, 2, 200, 700, 128
     q, k, v, _ = make_inputs("alt/paged", B, Hq, Hkv, Tq, Tk, d, "bf16")
     tq, tk, tv = dev(q), dev(k), dev(v)
     kp, vp, table = _page(tk, tv, 128, seed=4)
     kw = dict(scale=scale_for(d), q_offset=Tk - Tq, causal=True, tiling=(64, 4))
-    say("alternating paged")
+    say("8-wave paged")
     o1, l1 = fa.forward(tq, tk, tv, **kw)
     o2, l2 = fa.forward_paged(tq, kp, vp, table, Tk=Tk, **kw)
     torch.cuda.synchronize()
     assert np.array_equal(bits(o1), bits(o2)) and np.array_equal(bits(l1), bits(l2))
 
 
-def test_alternating_varlen():
-    """Packed sequences (lengths 0, 1 and around the tile edges) through the alternating kernel:
-    each sequence equals its own call bit for bit and the oracle within tolerance."""
+def test_eight_waves_varlen():
+    """Packed sequences (lengths 0, 1 and around the tile edges) with an 8-wave tiling: each
+    sequence equals its own call bit for bit and the oracle within tolerance."""
     from test_gpu_varlen import _check
     lens = [1, 63, 64, 65, 300, 0, 129, 200]
     _check(lens, lens, 8, 2, 128, "bf16", True, 0, True, 0, "alt/varlen", tiling=(64, 4))
+
+
+@pytest.mark.parametrize("tiling", [(32, 4), (64, 4)])
+def test_one_visible_key_returns_its_value(tiling):
+    """bf16: the denominator sums the weights as rounded for the PV product, so a row that sees
+    exactly one key (causal row 0, no sink) returns that key's value exactly, and a row that
+    sees two returns a convex combination of theirs (each output element between the two)."""
+    B, Hq, Hkv, Tq, Tk, d = 2, 8, 2, 64, 64, 128
+    q, k, v, _ = make_inputs("alt/one_key", B, Hq, Hkv, Tq, Tk, d, "bf16")
+    tq, tk, tv = dev(q), dev(k), dev(v)
+    say("one visible key", tiling)
+    o, _ = fa.forward(tq, tk, tv, scale=scale_for(d), causal=True, tiling=tiling)
+    torch.cuda.synchronize()
+    group = Hq // Hkv
+    for h in range(Hq):
+        kv = v[:, h // group].view(np.int16) if v.dtype == np.uint16 else None
+        assert np.array_equal(o[:, h, 0].view(torch.int16).cpu().numpy(), kv[:, 0]), f"head {h}"
+    vf = host(tv)
+    o1 = host(o[:, :, 1])
+    for h in range(Hq):
+        lo = np.minimum(vf[:, h // group, 0], vf[:, h // group, 1])
+        hi = np.maximum(vf[:, h // group, 0], vf[:, h // group, 1])
+        assert np.all(o1[:, h] >= lo) and np.all(o1[:, h] <= hi), f"head {h}"
