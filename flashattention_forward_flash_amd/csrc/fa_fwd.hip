@@ -62,8 +62,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.f;  // base-2 headroom before the running maximum is moved
 constexpr float kLazyW = 256.f;  // 2^kLazy
 #ifndef FA_QK_LOOKAHEAD
-#define FA_QK_LOOKAHEAD 2  // QK steps the K operand reads run ahead of the MFMAs
+#define FA_QK_LOOKAHEAD 2  // QK steps the K operand reads run ahead of the MFMAs (at most 6)
 #endif
+static_assert(FA_QK_LOOKAHEAD >= 1 && FA_QK_LOOKAHEAD <= 6, "2 reads per step, at most 15 LDS reads in flight");
 
 struct Params {
   const void *q, *k, *v;
@@ -236,10 +237,17 @@ __device__ __forceinline__ BufRsrc make_rsrc(const unsigned char *base, int64_t 
 __device__ __forceinline__ void buf_load_lds16(BufRsrc rs, unsigned char *lds_block, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds_block, 16, off, 0, 0, 0);
 }
+// The same copy as a global load that writes LDS (global_load_lds_dwordx4): cheaper to issue,
+// but without a range check, so only for bytes known to lie inside the tensor.
+__device__ __forceinline__ void glb_load_lds16(const unsigned char *base, unsigned char *lds_block, uint32_t off) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(base + off),
+                                   (__attribute__((address_space(3))) void *)lds_block, 16, 0, 0);
+}
 #else
 typedef int BufRsrc;
 __device__ inline BufRsrc make_rsrc(const unsigned char *, int64_t) { return 0; }
 __device__ inline void buf_load_lds16(BufRsrc, unsigned char *, uint32_t) {}
+__device__ inline void glb_load_lds16(const unsigned char *, unsigned char *, uint32_t) {}
 #endif
 
 
@@ -478,13 +486,16 @@ struct Wave {
         if (ds + KLA < NDS) issue(ds + KLA);
         hook(ds);
         // reads issued after step ds's: 2 per later step already in flight
-        constexpr int dummy = 0;
-        (void)dummy;
         const int ahead = (NDS - 1 - ds) < KLA ? (NDS - 1 - ds) : KLA;
-        if (ahead >= 3) lds_wait<6>(kc[0], kc[1]);
-        else if (ahead == 2) lds_wait<4>(kc[0], kc[1]);
-        else if (ahead == 1) lds_wait<2>(kc[0], kc[1]);
-        else lds_wait<0>(kc[0], kc[1]);
+        switch (ahead) {
+          case 0: lds_wait<0>(kc[0], kc[1]); break;
+          case 1: lds_wait<2>(kc[0], kc[1]); break;
+          case 2: lds_wait<4>(kc[0], kc[1]); break;
+          case 3: lds_wait<6>(kc[0], kc[1]); break;
+          case 4: lds_wait<8>(kc[0], kc[1]); break;
+          case 5: lds_wait<10>(kc[0], kc[1]); break;
+          default: lds_wait<12>(kc[0], kc[1]); break;
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
           dst[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kc[kb]), qb[ds], dst[kb], 0, 0, 0);
@@ -919,28 +930,35 @@ struct Copier {
   // each lane's.  Contiguous: the slice and the tile's place in it (rows past Tk lie past the
   // slice's end and read zeros; the host keeps a slice under 2 GiB, so the offsets fit 32
   // bits); paged: the tile's own resource.
+  // `inside`: a contiguous tile wholly inside the keys, which global loads may read.
   struct Src {
     BufRsrc rs;
     uint32_t add;
+    bool inside;
   };
   template <bool IS_K>
   __device__ __forceinline__ Src src(const Params &p, int t) const {
-    if (bt_row) return Src{paged_rsrc<IS_K>(p, t), 0u};
-    return Src{IS_K ? kslice : vslice, (uint32_t)t * (IS_K ? kstep : vstep)};
+    if (bt_row) return Src{paged_rsrc<IS_K>(p, t), 0u, false};
+    return Src{IS_K ? kslice : vslice, (uint32_t)t * (IS_K ? kstep : vstep), (int64_t)t * kBc + kBc <= p.Tk};
   }
-  // K copy i (of BPW) and V copy i of a tile from its sources.
+  // K copy i (of BPW) and V copy i of a tile from its sources; GLB: by global loads (the tile
+  // must be `inside`), else through the buffer resource.
+  template <bool GLB>
   __device__ __forceinline__ void copy_k(const Src &s, int i, unsigned char *kdst) const {
-    buf_load_lds16(s.rs, kdst + (wid * BPW + i) * 1024, koff[i] + s.add);
+    if constexpr (GLB) glb_load_lds16(kbase, kdst + (wid * BPW + i) * 1024, koff[i] + s.add);
+    else buf_load_lds16(s.rs, kdst + (wid * BPW + i) * 1024, koff[i] + s.add);
   }
+  template <bool GLB>
   __device__ __forceinline__ void copy_v(const Src &s, int i, unsigned char *vdst) const {
-    buf_load_lds16(s.rs, vdst + (wid * BPW + i) * 1024, voff[i] + s.add);
+    if constexpr (GLB) glb_load_lds16(vbase, vdst + (wid * BPW + i) * 1024, voff[i] + s.add);
+    else buf_load_lds16(s.rs, vdst + (wid * BPW + i) * 1024, voff[i] + s.add);
   }
   __device__ __forceinline__ void tiles(const Params &p, int t, unsigned char *kdst, unsigned char *vdst) const {
     const Src ks = src<true>(p, t), vs = src<false>(p, t);
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) copy_k(ks, i, kdst);
+    for (int i = 0; i < BPW; ++i) copy_k<false>(ks, i, kdst);
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) copy_v(vs, i, vdst);
+    for (int i = 0; i < BPW; ++i) copy_v<false>(vs, i, vdst);
   }
 };
 
@@ -1028,8 +1046,12 @@ fa_fwd_kernel(Params p0) {
     wv.mask_lds_row = (uint32_t)((wid / G) * kRowsWave + (lane & 31));
   }
 
-  auto step = [&](int t, const unsigned char *kc, const unsigned char *vc, const unsigned char *mcur,
-                  unsigned char *kn, unsigned char *vn, unsigned char *mnext) {
+  // GLB: the next tile's copies by global loads (every tile the work item copies lies wholly
+  // inside contiguous keys), else through the buffer resources.  Chosen once per work item, so
+  // that neither a copy nor a step carries a branch of its own.
+  auto step = [&](auto glb, int t, const unsigned char *kc, const unsigned char *vc, const unsigned char *mcur,
+                  unsigned char *kn, unsigned char *vn, unsigned char *mnext) __attribute__((always_inline)) {
+    constexpr bool GLB = decltype(glb)::value;
     const bool has_next = t + 1 < wk.t_end;  // the buffers kn, vn were released by the last barrier
     const typename CP::Src ks = cp.template src<true>(p, t + 1), vs = cp.template src<false>(p, t + 1);
     BufRsrc mrs;
@@ -1039,8 +1061,8 @@ fa_fwd_kernel(Params p0) {
 #pragma unroll
         for (int i = 0; i < NCP; ++i)
           if (i * NDS / NCP == ds) {
-            if (i < CP::BPW) cp.copy_k(ks, i, kn);
-            else cp.copy_v(vs, i - CP::BPW, vn);
+            if (i < CP::BPW) cp.template copy_k<GLB>(ks, i, kn);
+            else cp.template copy_v<GLB>(vs, i - CP::BPW, vn);
           }
         if (mlds) {
 #pragma unroll
@@ -1070,10 +1092,15 @@ fa_fwd_kernel(Params p0) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  for (int t = wk.t_begin; t < wk.t_end; t += 2) {
-    step(t, k0, v0, m0, k1, v1, m1);
-    if (t + 1 < wk.t_end) step(t + 1, k1, v1, m1, k0, v0, m0);
-  }
+  auto run = [&](auto glb) __attribute__((always_inline)) {
+    for (int t = wk.t_begin; t < wk.t_end; t += 2) {
+      step(glb, t, k0, v0, m0, k1, v1, m1);
+      if (t + 1 < wk.t_end) step(glb, t + 1, k1, v1, m1, k0, v0, m0);
+    }
+  };
+  // (not for the additive mask, whose kernel has no registers to spare for a second loop)
+  if (MODE != 1 && cp.template src<true>(p, wk.t_end - 1).inside) run(std::integral_constant<bool, MODE != 1>{});
+  else run(std::false_type{});
   wv.finish(p, wk.b, head, wk.split);
 }
 
