@@ -26,7 +26,8 @@
 //    The reference point m moves only when a tile's maximum exceeds it by more than kLazy;
 //    alpha = exp2(m_old - m_new) is then exactly 1 when m does not move and 0 when m_old =
 //    -inf (the guards of "Fused attention and softmax", exact definition steps 2 and 5);
-//    lse = (m + log2 l) ln 2.
+//    lse = (m + log2 l) ln 2.  The row maximum is only taken when it could move m (see
+//    Wave::weights); for bf16 the denominator l sums the weights as rounded for the PV MFMA.
 //  * Compiled with -ffp-contract=off: every fused multiply-add is written out, so the same
 //    source line gives the same bits on every code path (boundary or interior tile).
 //  * The same kernel serves split-KV (a work item per query tile and key split, its row
