@@ -177,11 +177,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return lo | (hi << 16);
 }
 
-// tanh(u) for the softcap: the odd Taylor series through u^13 for |u| < 0.55 (truncation
-// < 4e-7 relative), 1 - 2 / (e^{2|u|} + 1) above (hardware exp2 and reciprocal; saturates to
-// 1), with the sign of u.
-__device__ __forceinline__ float tanh_f(float u) {
-  const float a = fabsf(u);
+// tanh(u) for the softcap: the odd Taylor series through u^13 for |u| < kTanhSeries
+// (truncation < 4e-7 relative), 1 - 2 / (e^{2|u|} + 1) above (hardware exp2 and reciprocal;
+// saturates to 1), with the sign of u.
+constexpr float kTanhSeries = 0.55f;
+__device__ __forceinline__ float tanh_series(float a) {  // a = |u| < kTanhSeries
   const float a2 = a * a;
   float poly = 21844.f / 6081075.f;
   poly = __builtin_fmaf(poly, a2, -1382.f / 155925.f);
@@ -189,10 +189,13 @@ __device__ __forceinline__ float tanh_f(float u) {
   poly = __builtin_fmaf(poly, a2, -17.f / 315.f);
   poly = __builtin_fmaf(poly, a2, 2.f / 15.f);
   poly = __builtin_fmaf(poly, a2, -1.f / 3.f);
-  poly = __builtin_fmaf(poly * a2, a, a);
+  return __builtin_fmaf(poly * a2, a, a);
+}
+__device__ __forceinline__ float tanh_f(float u) {
+  const float a = fabsf(u);
   const float e = __builtin_amdgcn_exp2f(a * (2.f * kLog2e));
   const float big = 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
-  return copysignf(a < 0.55f ? poly : big, u);
+  return copysignf(a < kTanhSeries ? tanh_series(a) : big, u);
 }
 
 // Maps the launch index to a work index so that consecutive work items (which share a KV
@@ -610,10 +613,28 @@ struct Wave {
       return __builtin_fmaf(fabsf(d0 - off), al_slope, x);
     };
     if (p.cap_out > 0.f) {
+      // When no argument of the wave reaches the series' bound this tile, tanh_f would take the
+      // series everywhere: the exponential branch is left out (same bits).  The largest |s|
+      // decides, since |s cap_in| rounds monotonically in |s|.
+      float smax = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sc[kb][i] = biased(tanh_f(sc[kb][i] * p.cap_in) * p.cap_out, kb, i);
+        for (int i = 0; i < 16; ++i) smax = fmaxf(smax, fabsf(sc[kb][i]));
+      if (__ballot(smax * fabsf(p.cap_in) >= kTanhSeries)) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sc[kb][i] = biased(tanh_f(sc[kb][i] * p.cap_in) * p.cap_out, kb, i);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float u = sc[kb][i] * p.cap_in;
+            sc[kb][i] = biased(copysignf(tanh_series(fabsf(u)), u) * p.cap_out, kb, i);
+          }
+      }
     } else {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
