@@ -337,8 +337,11 @@ def bench_variants(steps=10, warmup=3):
 
 def sample_sclk(h, seconds=2.0):
     """The shader clock while the headline kernel runs back to back: `rocm-smi --showclocks`
-    polled from a host thread (MHz values seen; None where rocm-smi is unavailable)."""
+    polled from a host thread (MHz values seen; None where rocm-smi is unavailable, and under
+    a profiler whose preloaded library would start the GPU in every child process)."""
     import subprocess
+    if "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        return None
     import threading
     import torch
     import flashattention_forward_flash_amd as fa
