@@ -414,8 +414,8 @@ def main():
                     help="only run a 1 GiB device copy (reference for the memory counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (the pass shards over (b, head group) or "
-              "query tiles with no exchange; multi-GPU runs are not part of it). Use --gpus 1.",
+        print("bench.py measures one GPU only (the pass would shard over (b, head group) or query "
+              "tiles with no exchange between GPUs; runs on several GPUs are not supported). Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:

@@ -70,6 +70,11 @@ def load_library(path=None):
     if not os.path.exists(p):
         raise ImportError(f"{p} is missing: build it with `python -m flashattention_forward_flash_amd.build` "
                           "(there is no fallback path)")
+    # torch carries its own HIP runtime.  Imported first, it is the one the library binds to
+    # (the dynamic linker reuses the loaded libamdhip64), so torch's streams and allocations are
+    # valid in the library's calls.  Loaded the other way round, the process would hold two HIP
+    # runtimes and every launch on a torch stream would fail.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(p)
     lib.fa_fwd.restype = ctypes.c_int
     lib.fa_fwd.argtypes = _FWD_ARGS

@@ -1256,8 +1256,9 @@ bool aligned(const void *ptr, int64_t a) { return (reinterpret_cast<uintptr_t>(p
 
 // Picks (rows_per_block, heads_per_block): prefer 4 waves (8 measure the same or up to 1 %
 // slower) with as many heads of one KV group as divide the group, and fall back to fewer waves
-// per workgroup when that leaves the 256 CUs with too few workgroups.  Any choice gives the
-// same bits.
+// per workgroup only when 4-wave workgroups would leave some of the 256 CUs without one (at
+// one workgroup per CU, 4 waves sharing each staged tile beat twice as many 2-wave workgroups:
+// ≈ 20 % on a 2,044-token, 16-head causal prefill).  Any choice gives the same bits.
 void auto_tiling(int64_t B, int64_t Hkv, int64_t group, int64_t Tq, int32_t *rows, int32_t *heads) {
   for (int nw = 4; nw >= 1; nw /= 2) {
     int g = 1;
@@ -1265,7 +1266,7 @@ void auto_tiling(int64_t B, int64_t Hkv, int64_t group, int64_t Tq, int32_t *row
       if (group % c == 0) { g = c; break; }
     const int64_t r = 32 * nw / g;
     const int64_t blocks = B * Hkv * (group / g) * ((Tq + r - 1) / r);
-    if (blocks >= 512 || nw == 1) {
+    if (blocks >= 256 || nw == 1) {
       *heads = g;
       *rows = (int32_t)r;
       return;

@@ -4,10 +4,12 @@ include/fa.h declares, and rejects bad arguments before any launch.
 Every call here is one that must fail validation (or has no rows, so nothing is launched):
 no call may reach a kernel launch with these placeholder pointers.
 """
+import ast
 import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -32,6 +34,18 @@ def test_library_exports_every_declared_symbol():
     nm = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True, text=True, check=True)
     exported = set(re.findall(r" T (\w+)$", nm.stdout, re.M))
     assert set(names) <= exported
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """torch carries its own HIP runtime: loading the library before importing torch must still
+    leave one runtime in the process, or launches on torch's streams fail."""
+    code = ("import re, sys; sys.path.insert(0, %r); import flashattention_forward_flash_amd as fa; "
+            "fa.load_library(); import torch; "
+            "print(sorted(set(re.findall(r'\\S*libamdhip64\\S*', open('/proc/self/maps').read()))))") % ROOT
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True,
+                         timeout=300).stdout
+    runtimes = ast.literal_eval(out.strip().splitlines()[-1])
+    assert len(runtimes) == 1, runtimes
 
 
 def test_status_strings():
