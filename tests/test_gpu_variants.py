@@ -91,3 +91,32 @@ def test_variant_chunk_tiling_paged_bitwise(dtype):
     o2, l2 = fa.forward_paged(tq, kp, vp, table, Tk=T, **kw)
     torch.cuda.synchronize()
     assert np.array_equal(bits(o_full), bits(o2)) and np.array_equal(bits(l_full), bits(l2))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mask_free_variant_kernels_match_the_general_one(dtype, d):
+    """Without a mask, bf16 softcap calls run a softcap kernel and ALiBi-only calls an ALiBi
+    kernel with no mask code; an all-zero mask sends the same call to the general variant
+    kernel.  Adding 0 changes no score, so every tiling (4 and 8 waves, and 1 wave, which always
+    takes the general kernel) must give the bits of the masked call, which in turn matches the
+    oracle."""
+    Hq, Hkv, T = 8, 2, 300
+    q, k, v, z = make_inputs(f"variants/maskfree/{dtype}/{d}", 1, Hq, Hkv, T, T, d, dtype, sinks=True)
+    tq, tk, tv, tz = dev(q), dev(k), dev(v), dev(z)
+    zero = torch.zeros((T, T), dtype=torch.float32, device="cuda")
+    al = alibi_slopes(Hq)
+    for cap, with_alibi in ((10.0, False), (0.0, True), (10.0, True)):
+        kw = dict(scale=scale_for(d), causal=True, window=220, sinks=tz, softcap=cap,
+                  alibi_slopes=dev(al) if with_alibi else None)
+        say("mask-free variants", dtype, d, dict(softcap=cap, alibi=with_alibi))
+        o_m, l_m = fa.forward(tq, tk, tv, mask=zero, **kw)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.attention(q, k, v, scale=kw["scale"], causal=True, window=220, sinks=z, softcap=cap,
+                                        alibi=al if with_alibi else None)
+        compare(host(o_m), host(l_m), o_ref, l_ref, dtype, f"zero mask softcap {cap} alibi {with_alibi}")
+        for tiling in (None, (32, 4), (64, 4), (32, 1)):
+            o, lse = fa.forward(tq, tk, tv, tiling=tiling, **kw)
+            torch.cuda.synchronize()
+            assert np.array_equal(bits(o), bits(o_m)), f"O softcap {cap} alibi {with_alibi} tiling {tiling}"
+            assert np.array_equal(bits(lse), bits(l_m)), f"LSE softcap {cap} alibi {with_alibi} tiling {tiling}"
