@@ -1335,7 +1335,9 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   if (Hkv > Hq || (Hkv > 0 && Hq % Hkv != 0)) return FA_ESHAPE;
   if (dtype != FA_F32 && dtype != FA_BF16) return FA_EUNSUPPORTED;
   if (d != 64 && d != 128) return FA_EUNSUPPORTED;
-  const int64_t rows_total = B * Hq * Tq;
+  // the kernels keep B and Hq in 32 bits; B * Hq * Tq must not overflow
+  int64_t rows_total = 0;
+  if (B > INT32_MAX || Hq > INT32_MAX || __builtin_mul_overflow(B * Hq, Tq, &rows_total)) return FA_EUNSUPPORTED;
   if (rows_total > 0 && (q == nullptr || o == nullptr)) return FA_EINVAL;
   if (rows_total > 0 && Tk > 0 && (k == nullptr || v == nullptr)) return FA_EINVAL;
   // int32 limits of the kernel's row/key indices and of the 1-D grid
@@ -1569,7 +1571,8 @@ int64_t fa_splitkv_default_keys(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, 
 size_t fa_splitkv_workspace_bytes(int64_t B, int64_t Hq, int64_t Tq, int64_t Tk, int64_t d,
                                   int64_t split_keys) {
   if (B < 0 || Hq < 0 || Tq < 0 || Tk < 0 || d <= 0 || split_keys <= 0) return 0;
-  const int64_t rows = B * Hq * Tq;
+  int64_t rows = 0;
+  if (__builtin_mul_overflow(B, Hq, &rows) || __builtin_mul_overflow(rows, Tq, &rows)) return 0;
   const int64_t ns = n_splits_of(Tk, split_keys);
   if (rows > 0 && (ns > INT64_MAX / (4 * (d + 2)) / rows)) return 0;
   return (size_t)(ns * rows * (d + 2) * 4);

@@ -84,6 +84,9 @@ def _call(**kw):
     (dict(k=P + 4), fa.FA_EUNSUPPORTED),
     (dict(o=P + 8, dtype=fa.FA_F32), fa.FA_EUNSUPPORTED),
     (dict(Tq=2**31), fa.FA_EUNSUPPORTED),
+    (dict(B=2**31), fa.FA_EUNSUPPORTED),
+    (dict(Hq=2**31, Hkv=1), fa.FA_EUNSUPPORTED),
+    (dict(B=2**30, Hq=2**30, Hkv=2**30, Tq=2**10), fa.FA_EUNSUPPORTED),  # B * Hq * Tq overflows
 ])
 def test_validation_errors(kw, want):
     assert _call(**kw) == want
@@ -131,6 +134,9 @@ def test_splitkv_workspace_bytes():
     assert fa.fa_splitkv_workspace_bytes(1, 4, 0, 100, 128, 64) == 0
     assert fa.fa_splitkv_workspace_bytes(1, 4, 3, 100, 128, 0) == 0
     assert fa.fa_splitkv_workspace_bytes(-1, 4, 3, 100, 128, 64) == 0
+    assert fa.fa_splitkv_workspace_bytes(2**40, 2**40, 1, 100, 128, 64) == 0  # B * Hq overflows
+    assert fa.fa_splitkv_workspace_bytes(2**30, 2**30, 2**10, 100, 128, 64) == 0  # ... times Tq
+    assert fa.fa_splitkv_workspace_bytes(2**20, 2**20, 2**20, 100, 128, 64) == 0  # bytes overflow
 
 
 def test_splitkv_default_keys():
