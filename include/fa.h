@@ -201,7 +201,10 @@ size_t fa_splitkv_workspace_bytes(int64_t B, int64_t Hq, int64_t Tq, int64_t Tk,
  *   must be given.  Row i of sequence b sits at p_i = n_b - m_b + i (p_i = i when m_b = n_b)
  *   and q_offset must be 0.  cu_seqlens_k excludes seqlens_k and paging (which take their key
  *   counts from seqlens_k).  Every row equals a single-sequence fa_fwd call on its own
- *   tokens with q_offset = n_b - m_b, bit for bit.
+ *   tokens with q_offset = n_b - m_b, bit for bit.  The offsets live in device memory, so
+ *   the library cannot check them: lengths are clamped to [0, Tq] and [0, Tk], but offsets
+ *   that put a sequence's tokens outside q, k, v, o or lse make the kernels read or write out
+ *   of bounds (the caller's error, as for any pointer argument).
  *
  * Score variants (the candle page, "KV 缓存与注意力", attention/: variants with ALiBi and
  *   softcap; their usual definitions): softcap c > 0 turns the logit x = scale * q.k into
