@@ -20,7 +20,9 @@ The same JSON line also reports
     8,192 tokens;
   * cpu_baseline: the fp64 oracle timed on the host cores over a bounded row sample of the
     headline workload;
-  * sclk_during_headline: the shader clock rocm-smi reports while the headline kernel runs.
+  * sclk_during_headline: the shader clock rocm-smi reports while the headline kernel runs;
+  * inputs_sha256_16 (and mask_sha256_16 of the mask run): digests of the seeded host inputs,
+    the same on every run and box.
 """
 import argparse
 import hashlib
@@ -92,17 +94,24 @@ def _dev(a):
     return torch.from_numpy(a).cuda()
 
 
-def _inputs(tag, B, Hq, Hkv, Tq, Tk, d, dtype, layout="bhsd"):
+def _digest(a):
+    """sha256[:16] of a host array's bytes (the seeded inputs are the same on every run)."""
+    return hashlib.sha256(np.ascontiguousarray(a).view(np.uint8)).hexdigest()[:16]
+
+
+def _inputs(tag, B, Hq, Hkv, Tq, Tk, d, dtype, layout="bhsd", digests=None):
+    """Seeded N(0, 1) q, k, v on the GPU; `digests` (a dict) receives their sha256[:16]."""
     import synth
     if layout == "bshd":
-        q = synth.normal(synth.seed_of(tag, "q"), (B, Tq, Hq, d), dtype)
-        k = synth.normal(synth.seed_of(tag, "k"), (B, Tk, Hkv, d), dtype)
-        v = synth.normal(synth.seed_of(tag, "v"), (B, Tk, Hkv, d), dtype)
-        return tuple(_dev(a).transpose(1, 2) for a in (q, k, v))
-    q = synth.normal(synth.seed_of(tag, "q"), (B, Hq, Tq, d), dtype)
-    k = synth.normal(synth.seed_of(tag, "k"), (B, Hkv, Tk, d), dtype)
-    v = synth.normal(synth.seed_of(tag, "v"), (B, Hkv, Tk, d), dtype)
-    return _dev(q), _dev(k), _dev(v)
+        shapes = ((B, Tq, Hq, d), (B, Tk, Hkv, d), (B, Tk, Hkv, d))
+    else:
+        shapes = ((B, Hq, Tq, d), (B, Hkv, Tk, d), (B, Hkv, Tk, d))
+    arrs = [synth.normal(synth.seed_of(tag, n), sh, dtype) for n, sh in zip("qkv", shapes)]
+    if digests is not None:
+        digests.update({n: _digest(a) for n, a in zip("qkv", arrs)})
+    if layout == "bshd":
+        return tuple(_dev(a).transpose(1, 2) for a in arrs)
+    return tuple(_dev(a) for a in arrs)
 
 
 def _timed(fn, steps, warmup):
@@ -127,7 +136,8 @@ def bench_headline(steps, warmup):
     import torch
     import flashattention_forward_flash_amd as fa
     B, Hq, Hkv, T, d = 8, 32, 8, 8192, 128
-    q, k, v = _inputs("c5", B, Hq, Hkv, T, T, d, "bf16")
+    digests = {}
+    q, k, v = _inputs("c5", B, Hq, Hkv, T, T, d, "bf16", digests=digests)
     scale = float(np.float32(1 / math.sqrt(d)))
     out = torch.empty_like(q)
     lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
@@ -136,7 +146,7 @@ def bench_headline(steps, warmup):
     flops = 4.0 * d * B * Hq * visible_pairs(T, T)
     algo_bytes = 2 * (q.numel() + k.numel() + v.numel() + out.numel()) + 4 * lse.numel()
     return dict(B=B, Hq=Hq, Hkv=Hkv, T=T, d=d, flops=flops, bytes=algo_bytes, wall_ms=wall, event_ms=ev,
-                q=q, k=k, v=v, scale=scale)
+                q=q, k=k, v=v, scale=scale, digests=digests)
 
 
 def bench_mask_run(h, steps, warmup):
@@ -149,13 +159,14 @@ def bench_mask_run(h, steps, warmup):
     m = synth.neg_inf_mask(synth.seed_of("c5", "mask"), (T, T), 0.1)
     for r in (0, 1, 63, 64, 65, 127, 128, 1023, 1024, 2047, 4095, 4096, 6000, 8127, 8128, 8191):
         m[r] = -np.inf
+    digest = _digest(m)
     mask = torch.from_numpy(m).cuda()
     out = torch.empty_like(h["q"])
     print("[bench] headline inputs, non-causal, broadcast additive mask", file=sys.stderr, flush=True)
     wall, ev = _timed(lambda: fa.forward(h["q"], h["k"], h["v"], scale=h["scale"], causal=False, mask=mask,
                                          out=out), steps, warmup)
     flops = 4.0 * h["d"] * h["B"] * h["Hq"] * T * T
-    return dict(ms=ev, tflops=flops / (ev * 1e-3) / 1e12)
+    return dict(ms=ev, tflops=flops / (ev * 1e-3) / 1e12, mask_sha256_16=digest)
 
 
 def bench_prefill(T, dtype, layers=28, reps=5, split=False):
@@ -452,6 +463,7 @@ def main():
         "kernel_source_sha256_16": kernel_source_hash(),
         "kernel_ms": round(h["event_ms"], 4),
         "algorithmic_bytes": h["bytes"],
+        "inputs_sha256_16": h["digests"],
     }
     clk = sample_sclk(h)
     result["sclk_during_headline"] = clk
@@ -460,7 +472,8 @@ def main():
     if not args.headline_only:
         m = bench_mask_run(h, max(3, args.steps // 4), 2)
         result["mask_run"] = {"ms": round(m["ms"], 4), "tflops": round(m["tflops"], 2),
-                              "frac_mfma_peak": round(m["tflops"] / PEAK_BF16_TFLOPS, 4)}
+                              "frac_mfma_peak": round(m["tflops"] / PEAK_BF16_TFLOPS, 4),
+                              "mask_sha256_16": m["mask_sha256_16"]}
         torch.cuda.empty_cache()
         result["prefill_ms"] = {
             "511_f32_28L": bench_prefill(511, "f32"),
