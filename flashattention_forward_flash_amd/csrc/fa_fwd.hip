@@ -683,14 +683,17 @@ struct Wave {
       // mean of the values with weights summing to one (a row that sees one key gets that key's
       // value exactly): pairs of bf16 weights by dot products with (1, 1), 16 keys per chain,
       // the chains added in a fixed order.
+      // (Each chain starts with the three-operand form and an inline 0 addend, written out: the
+      // compiler would otherwise zero four registers for the accumulating two-operand form.)
       const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      float acc[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const bf16x2 pr = {pb[c][2 * j], pb[c][2 * j + 1]};
-          acc[c] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc[c], false);
+          if (j == 0) asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(acc[c]) : "v"(pr), "v"(one));
+          else acc[c] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc[c], false);
         }
       lsum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     } else {
@@ -966,24 +969,35 @@ struct Copier {
     if (bt_row) return Src{paged_rsrc<IS_K>(p, t), 0u, false};
     return Src{IS_K ? kslice : vslice, (uint32_t)t * (IS_K ? kstep : vstep), (int64_t)t * kBc + kBc <= p.Tk};
   }
-  // K copy i (of BPW) and V copy i of a tile from its sources; GLB: by global loads (the tile
-  // must be `inside`), else through the buffer resource.
+  // This wave's byte offset into a tile's LDS buffer.  Passed through an empty asm statement
+  // where a tile's copies are issued, so that the compiler forms each copy's LDS address
+  // (a scalar add) there instead of keeping all of them live in SGPRs across the tile loop,
+  // which runs out of SGPRs and spills them to VGPR lanes (a v_readlane per copy).
+  __device__ __forceinline__ uint32_t wave_off() const {
+    uint32_t w = (uint32_t)(wid * BPW * 1024);
+    asm volatile("" : "+s"(w));
+    return w;
+  }
+  // K copy i (of BPW) and V copy i of a tile from its sources into the LDS buffer at kdst / vdst
+  // (wo = wave_off()); GLB: by global loads (the tile must be `inside`), else through the
+  // buffer resource.
   template <bool GLB>
-  __device__ __forceinline__ void copy_k(const Src &s, int i, unsigned char *kdst) const {
-    if constexpr (GLB) glb_load_lds16(kbase, kdst + (wid * BPW + i) * 1024, koff[i] + s.add);
-    else buf_load_lds16(s.rs, kdst + (wid * BPW + i) * 1024, koff[i] + s.add);
+  __device__ __forceinline__ void copy_k(const Src &s, int i, unsigned char *kdst, uint32_t wo) const {
+    if constexpr (GLB) glb_load_lds16(kbase, kdst + wo + i * 1024, koff[i] + s.add);
+    else buf_load_lds16(s.rs, kdst + wo + i * 1024, koff[i] + s.add);
   }
   template <bool GLB>
-  __device__ __forceinline__ void copy_v(const Src &s, int i, unsigned char *vdst) const {
-    if constexpr (GLB) glb_load_lds16(vbase, vdst + (wid * BPW + i) * 1024, voff[i] + s.add);
-    else buf_load_lds16(s.rs, vdst + (wid * BPW + i) * 1024, voff[i] + s.add);
+  __device__ __forceinline__ void copy_v(const Src &s, int i, unsigned char *vdst, uint32_t wo) const {
+    if constexpr (GLB) glb_load_lds16(vbase, vdst + wo + i * 1024, voff[i] + s.add);
+    else buf_load_lds16(s.rs, vdst + wo + i * 1024, voff[i] + s.add);
   }
   __device__ __forceinline__ void tiles(const Params &p, int t, unsigned char *kdst, unsigned char *vdst) const {
     const Src ks = src<true>(p, t), vs = src<false>(p, t);
+    const uint32_t wo = wave_off();
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) copy_k<false>(ks, i, kdst);
+    for (int i = 0; i < BPW; ++i) copy_k<false>(ks, i, kdst, wo);
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) copy_v<false>(vs, i, vdst);
+    for (int i = 0; i < BPW; ++i) copy_v<false>(vs, i, vdst, wo);
   }
 };
 
@@ -1085,11 +1099,12 @@ fa_fwd_kernel(Params p0) {
     if (mlds) mrs = mc.rsrc(t + 1);
     auto copies = [&](int ds) {  // copy i goes with QK step i * NDS / NCP
       if (has_next) {
+        const uint32_t wo = cp.wave_off();
 #pragma unroll
         for (int i = 0; i < NCP; ++i)
           if (i * NDS / NCP == ds) {
-            if (i < CP::BPW) cp.template copy_k<GLB>(ks, i, kn);
-            else cp.template copy_v<GLB>(vs, i - CP::BPW, vn);
+            if (i < CP::BPW) cp.template copy_k<GLB>(ks, i, kn, wo);
+            else cp.template copy_v<GLB>(vs, i - CP::BPW, vn, wo);
           }
         if (mlds) {
 #pragma unroll
