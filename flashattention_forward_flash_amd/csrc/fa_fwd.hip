@@ -979,16 +979,16 @@ struct Copier {
     return w;
   }
   // K copy i (of BPW) and V copy i of a tile from its sources into the LDS buffer at kdst / vdst
-  // (wo = wave_off()); GLB: by global loads (the tile must be `inside`), else through the
-  // buffer resource.
+  // (wo = wave_off()); GLB: by global loads from the tile's base address (the tile must be
+  // `inside`), else through the buffer resource.
   template <bool GLB>
   __device__ __forceinline__ void copy_k(const Src &s, int i, unsigned char *kdst, uint32_t wo) const {
-    if constexpr (GLB) glb_load_lds16(kbase, kdst + wo + i * 1024, koff[i] + s.add);
+    if constexpr (GLB) glb_load_lds16(kbase + s.add, kdst + wo + i * 1024, koff[i]);
     else buf_load_lds16(s.rs, kdst + wo + i * 1024, koff[i] + s.add);
   }
   template <bool GLB>
   __device__ __forceinline__ void copy_v(const Src &s, int i, unsigned char *vdst, uint32_t wo) const {
-    if constexpr (GLB) glb_load_lds16(vbase, vdst + wo + i * 1024, voff[i] + s.add);
+    if constexpr (GLB) glb_load_lds16(vbase + s.add, vdst + wo + i * 1024, voff[i]);
     else buf_load_lds16(s.rs, vdst + wo + i * 1024, voff[i] + s.add);
   }
   __device__ __forceinline__ void tiles(const Params &p, int t, unsigned char *kdst, unsigned char *vdst) const {
@@ -1094,6 +1094,16 @@ fa_fwd_kernel(Params p0) {
                   unsigned char *kn, unsigned char *vn, unsigned char *mnext) __attribute__((always_inline)) {
     constexpr bool GLB = decltype(glb)::value;
     const bool has_next = t + 1 < wk.t_end;  // the buffers kn, vn were released by the last barrier
+    if constexpr (GLB) {
+      // The lanes' copy offsets pass through empty asm statements once per tile, so that the
+      // compiler cannot hoist their 64-bit forms out of the loop: each global copy then takes
+      // the tile's base address from SGPRs and the 32-bit lane offset as is (no vector add).
+#pragma unroll
+      for (int i = 0; i < CP::BPW; ++i) {
+        asm("" : "+v"(cp.koff[i]));
+        asm("" : "+v"(cp.voff[i]));
+      }
+    }
     const typename CP::Src ks = cp.template src<true>(p, t + 1), vs = cp.template src<false>(p, t + 1);
     BufRsrc mrs;
     if (mlds) mrs = mc.rsrc(t + 1);
