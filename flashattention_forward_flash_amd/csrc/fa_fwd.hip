@@ -26,8 +26,11 @@
 //    The reference point m moves only when a tile's maximum exceeds it by more than kLazy;
 //    alpha = exp2(m_old - m_new) is then exactly 1 when m does not move and 0 when m_old =
 //    -inf (the guards of "Fused attention and softmax", exact definition steps 2 and 5);
-//    lse = (m + log2 l) ln 2.  The row maximum is only taken when it could move m (see
-//    Wave::weights); for bf16 the denominator l sums the weights as rounded for the PV MFMA.
+//    lse = (m + log2 l) ln 2.  fp32 kernels take the row maximum only when it could move m
+//    (Wave::weights).  bf16 kernels take it first and then, per 16-key chunk, compute the
+//    weights and issue that chunk's PV MFMAs, which run while the next chunk's weights are
+//    computed (Wave::softmax_pv); their denominator l sums the weights as rounded for the PV
+//    MFMA.
 //  * Compiled with -ffp-contract=off: every fused multiply-add is written out, so the same
 //    source line gives the same bits on every code path (boundary or interior tile).
 //  * The same kernel serves split-KV (a work item per query tile and key split, its row
@@ -656,9 +659,10 @@ struct Wave {
       }
   }
 
-  // The tile's weights exp2(x - shift) in base-2 units (the B operand of the PV MFMAs) and this
-  // half's partial denominator.
+  // fp32 kernels: the tile's weights exp2(x - shift) in base-2 units (the B operand of the PV
+  // MFMAs) and this half's partial denominator.
   __device__ __forceinline__ float expw(const Params &p, const f32x16 (&sc)[2], float shift) {
+    static_assert(!BF16, "bf16 kernels take softmax_pv");
     float w[2][16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -671,70 +675,25 @@ struct Wave {
         else
           w[kb][i] = __builtin_amdgcn_exp2f(sc[kb][i] - shift);
       }
-    float lsum;
-    if constexpr (BF16) {
-      // MFMA c covers keys 16c..16c+15; lane half h supplies keys 16c + 8(j/4) + 4h + j%4,
-      // which are its S^T registers i = 8(c%2) + j of block c/2.
+    float s8[8];
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+    for (int j = 0; j < 8; ++j)
+      s8[j] = (w[j >> 2][4 * (j & 3)] + w[j >> 2][4 * (j & 3) + 1]) +
+              (w[j >> 2][4 * (j & 3) + 2] + w[j >> 2][4 * (j & 3) + 3]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pb[c][j] = (__bf16)w[c >> 1][8 * (c & 1) + j];
-      // The denominator sums the weights as rounded for the PV product, so that o is a weighted
-      // mean of the values with weights summing to one (a row that sees one key gets that key's
-      // value exactly): pairs of bf16 weights by dot products with (1, 1), 16 keys per chain,
-      // the chains added in a fixed order.
-      // (Each chain starts with the three-operand form and an inline 0 addend, written out: the
-      // compiler would otherwise zero four registers for the accumulating two-operand form.)
-      const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
-      float acc[4];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bf16x2 pr = {pb[c][2 * j], pb[c][2 * j + 1]};
-          if (j == 0) asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(acc[c]) : "v"(pr), "v"(one));
-          else acc[c] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc[c], false);
-        }
-      lsum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    } else {
-      float s8[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        s8[j] = (w[j >> 2][4 * (j & 3)] + w[j >> 2][4 * (j & 3) + 1]) +
-                (w[j >> 2][4 * (j & 3) + 2] + w[j >> 2][4 * (j & 3) + 3]);
-      lsum = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) pw[kb][i] = w[kb][i];
-    }
-    return lsum;
+      for (int i = 0; i < 16; ++i) pw[kb][i] = w[kb][i];
+    return ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
   }
 
-  // Online-softmax step on the tile's scores: reference point m, denominator l and the weights.
-  // Returns alpha, the factor O^T must be multiplied by.
-  //
-  // The reference point moves only when the tile's row maximum exceeds it by more than kLazy
-  // (base-2 units), or m is still -inf: weights are then exp2(x - m) <= 2^kLazy, and most
-  // tiles need no rescale.  The rule depends on the row's own scores only, so a row's bits stay
-  // independent of chunking and query tiling.
-  //
-  // MODE 0 and 1 first compute the weights against the current m.  When every lane's partial
-  // denominator stays below 2^kLazy and no m is -inf, every weight is below 2^kLazy, so every
-  // x - m is below kLazy (exp2 and the bf16 rounding are monotonic and exact at 2^kLazy) and
-  // the rule keeps m: those weights are the tile's, and the row maximum is never taken.
-  // Otherwise the maximum decides as stated, and the weights are recomputed for the rows whose
-  // m moved.  Both ways give the same bits.  MODE 2-4 take the maximum first: under ALiBi the
-  // reference point of many rows moves at every tile.
-  __device__ __forceinline__ float weights(const Params &p, const f32x16 (&sc)[2]) {
-    float lsum = 0.f;
-    if constexpr (MODE < 2) {
-      lsum = expw(p, sc, m_run == -INFINITY ? 0.f : m_run);
-      if (!__ballot(m_run == -INFINITY || !(lsum < kLazyW))) {
-        l_run = __builtin_fmaf(1.f, l_run, lsum);
-        return 1.f;
-      }
-    }
+  // The reference point m of the online softmax.  It moves only when the tile's row maximum
+  // exceeds it by more than kLazy (base-2 units), or m is still -inf: weights are then
+  // exp2(x - m) <= 2^kLazy, and most tiles need no rescale.  The rule depends on the row's own
+  // scores only, so a row's bits stay independent of chunking and query tiling.  Returns the
+  // new m; `shift` is the point weights are taken against, `alpha` the factor for O^T and l.
+  __device__ __forceinline__ float ref_point(const Params &p, const f32x16 (&sc)[2], float &shift,
+                                             float &alpha) const {
     // row maximum (exact, so the reduction order is immaterial)
     float mx = sc[0][0];
 #pragma unroll
@@ -751,8 +710,32 @@ struct Wave {
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       m_new = (mx > m_run + kLazy) ? mx : m_run;
     }
-    const float shift = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - shift);
+    shift = m_new == -INFINITY ? 0.f : m_new;
+    alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - shift);
+    return m_new;
+  }
+
+  // fp32 kernels: the online-softmax step on the tile's scores (reference point, denominator,
+  // weights).  Returns alpha, the factor O^T must be multiplied by.
+  //
+  // MODE 0 and 1 first compute the weights against the current m.  When every lane's partial
+  // denominator stays below 2^kLazy and no m is -inf, every weight is below 2^kLazy, so every
+  // x - m is below kLazy (exp2 is monotonic and exact at 2^kLazy) and the rule keeps m: those
+  // weights are the tile's, and the row maximum is never taken.  Otherwise the maximum decides,
+  // and the weights are recomputed for the rows whose m moved.  Both ways give the same bits.
+  // MODE 2-4 take the maximum first: under ALiBi the reference point of many rows moves at
+  // every tile.
+  __device__ __forceinline__ float weights(const Params &p, const f32x16 (&sc)[2]) {
+    float lsum = 0.f;
+    if constexpr (MODE < 2) {
+      lsum = expw(p, sc, m_run == -INFINITY ? 0.f : m_run);
+      if (!__ballot(m_run == -INFINITY || !(lsum < kLazyW))) {
+        l_run = __builtin_fmaf(1.f, l_run, lsum);
+        return 1.f;
+      }
+    }
+    float shift, alpha;
+    const float m_new = ref_point(p, sc, shift, alpha);
     if (MODE >= 2 || __ballot(m_new != m_run)) lsum = expw(p, sc, shift);
     l_run = __builtin_fmaf(alpha, l_run, lsum);
     m_run = m_new;
@@ -769,17 +752,27 @@ struct Wave {
     }
   }
 
-  // The whole online-softmax step of tile t on `sacc`.
+  // fp32 kernels: the whole online-softmax step of tile t on `sacc`, then pv().
   __device__ __forceinline__ void softmax(const Params &p, int t, const unsigned char *ml = nullptr) {
     scores(p, t, sacc, ml);
     if (!full(t)) select(t, sacc);
     rescale(weights(p, sacc));
   }
 
-  // O^T += V^T P^T with the tile's V in `vl`.  The MFMAs are ordered key block outer, d block
-  // inner, so that consecutive MFMAs accumulate into different registers.
-  __device__ __forceinline__ void pv(const unsigned char *vl) {
-    if constexpr (BF16) {
+  // bf16 kernels: the online-softmax step of tile t on `sacc` and O^T = alpha O^T + V^T P^T
+  // with the tile's V in `vl`, fused per 16-key chunk.  The reference point comes first (the
+  // row maximum, every tile); then chunk c's weights, their bf16 rounding and partial sums, and
+  // chunk c's PV MFMAs, whose execution overlaps the vector work of chunk c + 1.  The MFMAs are
+  // ordered key chunk outer, d block inner, so that consecutive MFMAs accumulate into different
+  // registers.
+  __device__ __forceinline__ void softmax_pv(const Params &p, int t, const unsigned char *ml,
+                                             const unsigned char *vl) {
+    scores(p, t, sacc, ml);
+    if (!full(t)) select(t, sacc);
+    float shift, alpha;
+    const float m_new = ref_point(p, sacc, shift, alpha);
+    rescale(alpha);
+    {
       // The V^T operand of MFMA c comes from two transposing reads: within each 16-lane group,
       // lane r reads 4 d of key 16c + 8e + 4h + r/4, and lane i receives keys ... + j
       // (j = 0..3) at one d.
@@ -799,9 +792,34 @@ struct Wave {
           r[c & 1][2 * db + 1] = read_v(a0[db], c, 1);
         }
       };
+      // The denominator sums the weights as rounded for the PV product, so that o is a weighted
+      // mean of the values with weights summing to one (a row that sees one key gets that key's
+      // value exactly): pairs of bf16 weights by dot products with (1, 1), one chain per chunk,
+      // the chains added in a fixed order.  (Each chain starts with the three-operand form and
+      // an inline 0 addend, written out: the compiler would otherwise zero a register for the
+      // accumulating two-operand form.)
+      const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+      float acc[4];
       issue(0);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
+        // chunk c covers keys 16c..16c+15; lane half h supplies keys 16c + 8(j/4) + 4h + j%4,
+        // which are its S^T registers i = 8(c%2) + j of block c/2
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x = sacc[c >> 1][8 * (c & 1) + j];
+          float w;
+          if constexpr (MODE == 0) w = __builtin_amdgcn_exp2f(__builtin_fmaf(x, p.scale_log2, -shift));
+          else if constexpr (MODE == 1) w = __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -shift));
+          else w = __builtin_amdgcn_exp2f(x - shift);
+          pb[c][j] = (__bf16)w;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x2 pr = {pb[c][2 * j], pb[c][2 * j + 1]};
+          if (j == 0) asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(acc[c]) : "v"(pr), "v"(one));
+          else acc[c] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc[c], false);
+        }
         s16x4 *rc = r[c & 1];
         if (c + 1 < 4) {  // the reads for key block c + 1 are in flight during the MFMAs of c
           issue(c + 1);
@@ -818,24 +836,30 @@ struct Wave {
                                                              oacc[db], 0, 0, 0);
         }
       }
-    } else {
-      // MFMA (kb, i) contracts 2 keys: lane half h supplies key 32kb + 8(i/4) + 4h + i%4.
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const int d = db * 32 + lq;
-            const int ch = (d >> 2) ^ L::vsw(key);
-            const float a = *reinterpret_cast<const float *>(vl + key * (D * 4) + ch * 16 + (d & 3) * 4);
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pw[kb][i], oacc[db], 0, 0, 0);
-          }
-        }
+      l_run = __builtin_fmaf(alpha, l_run, (acc[0] + acc[1]) + (acc[2] + acc[3]));
+      m_run = m_new;
     }
   }
-  // transposing read of keys 16c + 8e + key_l (immediate offset), see pv()
+
+  // fp32 kernels: O^T += V^T P^T with the tile's V in `vl`.  MFMA (kb, i) contracts 2 keys:
+  // lane half h supplies key 32kb + 8(i/4) + 4h + i%4.
+  __device__ __forceinline__ void pv(const unsigned char *vl) {
+    static_assert(!BF16, "bf16 kernels take softmax_pv");
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int d = db * 32 + lq;
+          const int ch = (d >> 2) ^ L::vsw(key);
+          const float a = *reinterpret_cast<const float *>(vl + key * (D * 4) + ch * 16 + (d & 3) * 4);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pw[kb][i], oacc[db], 0, 0, 0);
+        }
+      }
+  }
+  // transposing read of keys 16c + 8e + key_l (immediate offset), see softmax_pv()
   __device__ __forceinline__ static s16x4 read_v(uint32_t a, int c, int e) {
     switch (2 * c + e) {
       case 0: return lds_read_tr16<0 * D * 2>(a);
@@ -1125,8 +1149,12 @@ fa_fwd_kernel(Params p0) {
     };
     if (wv.active(t)) {
       wv.template qk<true>(kc, wv.sacc, copies);
-      wv.softmax(p, t, mcur);
-      wv.pv(vc);
+      if constexpr (BF16) {
+        wv.softmax_pv(p, t, mcur, vc);
+      } else {
+        wv.softmax(p, t, mcur);
+        wv.pv(vc);
+      }
     } else {
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) copies(ds);
