@@ -1317,19 +1317,21 @@ KernelFn pick_nw(int nw, int mode) {
 
 bool aligned(const void *ptr, int64_t a) { return (reinterpret_cast<uintptr_t>(ptr) % (uintptr_t)a) == 0; }
 
-// Picks (rows_per_block, heads_per_block): prefer 4 waves (8 measure the same or up to 1 %
-// slower) with as many heads of one KV group as divide the group, and fall back to fewer waves
-// per workgroup only when 4-wave workgroups would leave some of the 256 CUs without one (at
-// one workgroup per CU, 4 waves sharing each staged tile beat twice as many 2-wave workgroups:
-// ≈ 20 % on a 2,044-token, 16-head causal prefill).  Any choice gives the same bits.
-void auto_tiling(int64_t B, int64_t Hkv, int64_t group, int64_t Tq, int32_t *rows, int32_t *heads) {
-  for (int nw = 4; nw >= 1; nw /= 2) {
+// Picks (rows_per_block, heads_per_block): 4 waves with as many heads of one KV group as
+// divide the group, falling back to fewer waves per workgroup only when 4-wave workgroups
+// would leave some of the 256 CUs without one (at one workgroup per CU, 4 waves sharing each
+// staged tile beat twice as many 2-wave workgroups: ≈ 20 % on a 2,044-token, 16-head causal
+// prefill).  `eight`: the plain bf16 d = 128 kernel, whose 8-wave workgroups (one per CU, two
+// waves per SIMD) measure ≈ 1 % faster than two 4-wave ones when there are at least two
+// rounds of them.  Any choice gives the same bits.
+void auto_tiling(int64_t B, int64_t Hkv, int64_t group, int64_t Tq, bool eight, int32_t *rows, int32_t *heads) {
+  for (int nw = eight ? 8 : 4; nw >= 1; nw /= 2) {
     int g = 1;
     for (int c = nw; c >= 2; c /= 2)
       if (group % c == 0) { g = c; break; }
     const int64_t r = 32 * nw / g;
     const int64_t blocks = B * Hkv * (group / g) * ((Tq + r - 1) / r);
-    if (blocks >= 256 || nw == 1) {
+    if (blocks >= (nw == 8 ? 512 : 256) || nw == 1) {
       *heads = g;
       *rows = (int32_t)r;
       return;
@@ -1479,7 +1481,10 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
     return FA_EUNSUPPORTED;
   if (rows_pb == 0) {
     if (split) split_tiling(group, Tq, &rows_pb, &heads_pb);
-    else auto_tiling(B, Hkv, group, Tq, &rows_pb, &heads_pb);
+    else auto_tiling(B, Hkv, group, Tq,
+                     dtype == FA_BF16 && d == 128 && mask == nullptr && !(x.softcap > 0.f) && !x.alibi_slopes &&
+                         scale > 0.f,
+                     &rows_pb, &heads_pb);
   }
   const int nw = (int)((int64_t)rows_pb * heads_pb / 32);
   const int64_t n_row_tiles = (Tq + rows_pb - 1) / rows_pb;
