@@ -7,7 +7,9 @@ the scores, 2d for P V; exp, max and sum not counted) over the wall time of the 
 
 The same JSON line also reports
   * roofline: the kernel's average duration from HIP events on its stream, against the
-    MI355X dense bf16 MFMA peak;
+    MI355X dense bf16 MFMA peak; hbm_from_counters: the HBM bytes per launch that the committed
+    rocprofv3 counter summary measured (FETCH_SIZE, WRITE_SIZE, scaled by a plain copy), over
+    this run's launch time, when that summary was taken on the current kernel source;
   * prefill_ms: 28 back-to-back calls (one per layer, fresh seeded inputs per layer) at
     16 query / 8 KV heads, d 128: 511 tokens fp32, 2044 tokens fp32 and bf16; and
     prefill_ms_splitkv: the same through split-KV at the default split size (results within
@@ -465,6 +467,11 @@ def main():
         "algorithmic_bytes": h["bytes"],
         "inputs_sha256_16": h["digests"],
     }
+    traffic = result["roofline"]["traffic"]
+    if traffic:  # HBM bytes per launch from the rocprofv3 counters, over this run's launch time
+        gbs = traffic / (h["event_ms"] * 1e-3) / 1e9
+        result["hbm_from_counters"] = {"bytes_per_launch": traffic, "GBs": round(gbs, 1),
+                                       "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
     clk = sample_sclk(h)
     result["sclk_during_headline"] = clk
     if clk:  # the published peak assumes 2.4 GHz; the same fraction at the clock the box ran at
