@@ -373,11 +373,16 @@ struct Work {
 // One wave: 32 query rows of one head.  Holds the rows' Q (MFMA B operand), the O^T
 // accumulators and the online-softmax state, and does the per-tile math.
 // ---------------------------------------------------------------------------------------
-template <bool BF16, int D, int MODE>
+// DP > 1 (fp32 only): DP waves share one head's 32 rows, each computing the scores and weights
+// of every key and the output for its own D / DP of the d range (blocks of 32); every output
+// element has the arithmetic of DP = 1, so the bits do not change.
+template <bool BF16, int D, int MODE, int DP = 1>
 struct Wave {
   using L = Layout<BF16, D>;
   static constexpr int ES = L::ES;
   static constexpr int NDB = D / 32;  // 32-row blocks of O^T
+  static constexpr int NOB = NDB / DP;  // ... that this wave computes: dpart * NOB + [0, NOB)
+  static_assert(DP == 1 || (!BF16 && NDB % DP == 0), "d parts: fp32 kernels, whole blocks");
 
   int half, lq, lane, row;
   bool row_ok;
@@ -391,14 +396,16 @@ struct Wave {
   bf16x8 qb[BF16 ? D / 16 : 1];
   float qf[BF16 ? 1 : D / 2];
   float m_run, l_run;        // reference maximum (base-2 units) and this half's partial l
-  f32x16 oacc[NDB];
+  int dpart;                 // DP > 1: this wave's part of the d range
+  f32x16 oacc[NOB];
   f32x16 sacc[2];            // S^T of the current tile; lane holds key 32kb + 8(i/4) + 4 half + i%4
   bf16x8 pb[BF16 ? 4 : 1];   // bf16 weights, the B operand of the PV MFMAs
   float pw[BF16 ? 1 : 2][16];  // fp32 weights (fp32 path)
 
   __device__ __forceinline__ void init(const Params &p, int b, int head, int row0_wave, int lane_,
-                                       bool with_sink) {
+                                       bool with_sink, int dpart_ = 0) {
     lane = lane_;
+    dpart = dpart_;
     half = lane >> 5;
     lq = lane & 31;
     row = row0_wave + lq;
@@ -450,7 +457,7 @@ struct Wave {
       l_run = half == 0 ? 1.f : 0.f;
     }
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NOB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   }
@@ -746,7 +753,7 @@ struct Wave {
   __device__ __forceinline__ void rescale(float alpha) {
     if (__ballot(alpha != 1.f)) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NOB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
@@ -767,6 +774,7 @@ struct Wave {
   // registers.
   __device__ __forceinline__ void softmax_pv(const Params &p, int t, const unsigned char *ml,
                                              const unsigned char *vl) {
+    static_assert(DP == 1, "bf16 kernels own the whole d range");
     scores(p, t, sacc, ml);
     if (!full(t)) select(t, sacc);
     float shift, alpha;
@@ -851,8 +859,8 @@ struct Wave {
       for (int i = 0; i < 16; ++i) {
         const int key = kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int d = db * 32 + lq;
+        for (int db = 0; db < NOB; ++db) {
+          const int d = (dpart * NOB + db) * 32 + lq;
           const int ch = (d >> 2) ^ L::vsw(key);
           const float a = *reinterpret_cast<const float *>(vl + key * (D * 4) + ch * 16 + (d & 3) * 4);
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pw[kb][i], oacc[db], 0, 0, 0);
@@ -885,13 +893,13 @@ struct Wave {
       const int64_t r = ((int64_t)split * p.B * p.Hq + (int64_t)b * p.Hq + head) * p.Tq_all + row;
       float *arow = p.ws_acc + r * D;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NOB; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const f32x4 v4 = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
-          *reinterpret_cast<f32x4 *>(arow + db * 32 + 8 * g + 4 * half) = v4;
+          *reinterpret_cast<f32x4 *>(arow + (dpart * NOB + db) * 32 + 8 * g + 4 * half) = v4;
         }
-      if (half == 0) {
+      if (half == 0 && dpart == 0) {
         const f32x2 ml = {m_run, l_tot};
         *reinterpret_cast<f32x2 *>(p.ws_ml + 2 * r) = ml;
       }
@@ -902,10 +910,10 @@ struct Wave {
                           ((int64_t)b * p.so_b + (int64_t)head * p.so_h + (p.q_start + row) * p.so_t) * ES;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NOB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d0 = db * 32 + 8 * g + 4 * half;  // registers 4g..4g+3 hold d0..d0+3
+        const int d0 = (dpart * NOB + db) * 32 + 8 * g + 4 * half;  // registers 4g..4g+3 hold d0..d0+3
         float r4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) r4[e] = oacc[db][4 * g + e] * inv;
@@ -917,7 +925,7 @@ struct Wave {
           *reinterpret_cast<f32x4 *>(orow + d0 * 4) = v4;
         }
       }
-    if (p.lse && half == 0)
+    if (p.lse && half == 0 && dpart == 0)
       p.lse[(int64_t)b * p.sl_b + (int64_t)head * p.sl_h + p.q_start + row] =
           l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   }
@@ -1070,7 +1078,7 @@ struct MaskCopier {
 // 8-wave workgroups, which put 2 waves on each SIMD by construction.  The mask-free variant
 // kernels (MODE 3, 4) take 2: MODE 3 spills a few registers there and still runs ≈ 10 % faster
 // than at 1, MODE 4 ≈ 25 %.
-template <bool BF16, int D, int NW, int MODE>
+template <bool BF16, int D, int NW, int MODE, int DP = 1>
 __global__ void __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(MODE == 2 ? (NW == 8 ? 2 : 1) : (BF16 || NW == 8) ? 2 : 1)))
 fa_fwd_kernel(Params p0) {
@@ -1097,9 +1105,11 @@ fa_fwd_kernel(Params p0) {
   // states (split 0 keeps the sink term and always writes them)
   if (p.n_splits > 0 && wk.t_begin >= wk.t_end && (wk.split != 0 || p.sinks == nullptr)) return;
   const int G = p.heads_per_block;
-  const int head = wk.head_base + wid % G;
-  Wave<BF16, D, MODE> wv;
-  wv.init(p, wk.b, head, wk.row0_blk + (wid / G) * kRowsWave, lane, wk.split == 0);
+  // wave wid: part wid % DP of the d range, head wq % G, rows (wq / G) * 32 of the block
+  const int wq = wid / DP;
+  const int head = wk.head_base + wq % G;
+  Wave<BF16, D, MODE, DP> wv;
+  wv.init(p, wk.b, head, wk.row0_blk + (wq / G) * kRowsWave, lane, wk.split == 0, wid % DP);
   CP cp;
   cp.init(p, wk.b, wk.kvh, wid, lane);
   using MC = MaskCopier<NW>;
@@ -1108,7 +1118,7 @@ fa_fwd_kernel(Params p0) {
   const bool mlds = MODE == 1 && p.mask_lds;
   if (mlds) {
     mc.init(p, wk.b, wk.row0_blk, wid, lane);
-    wv.mask_lds_row = (uint32_t)((wid / G) * kRowsWave + (lane & 31));
+    wv.mask_lds_row = (uint32_t)((wq / G) * kRowsWave + (lane & 31));
   }
 
   // GLB: the next tile's copies by global loads (every tile the work item copies lies wholly
@@ -1479,6 +1489,7 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   if (Tk > 0 && !paged &&
       (((Tk - 1) * s.k[2] + d) * es >= INT32_MAX || ((Tk - 1) * s.v[2] + d) * es >= INT32_MAX))
     return FA_EUNSUPPORTED;
+  const bool auto_geom = rows_pb == 0 && !split;
   if (rows_pb == 0) {
     if (split) split_tiling(group, Tq, &rows_pb, &heads_pb);
     else auto_tiling(B, Hkv, group, Tq,
@@ -1546,8 +1557,17 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
                32 * s.mask[2] * 4 < INT32_MAX;
   KernelFn fn = bf16 ? (d == 64 ? pick_nw<true, 64>(nw, mode) : pick_nw<true, 128>(nw, mode))
                      : (d == 64 ? pick_nw<false, 64>(nw, mode) : pick_nw<false, 128>(nw, mode));
+  // A plain fp32 call that one-wave workgroups already spread over the CUs is bound by each
+  // wave's chain of fp32 MFMAs: there d / 32 waves share each 32-row block, every one computing
+  // the scores and weights and its own 32 columns of the output (the same bits, a chain
+  // shorter by 3/8 at d = 128: the 511-token, 16-head prefill takes ≈ 27 % less time).
+  int waves = nw;
+  if (auto_geom && !bf16 && mode == 0 && nw == 1) {
+    waves = (int)(d / 32);
+    fn = d == 64 ? fa_fwd_kernel<false, 64, 2, 0, 2> : fa_fwd_kernel<false, 128, 4, 0, 4>;
+  }
   (void)hipGetLastError();  // clear a stale error so the check below reports this launch
-  hipLaunchKernelGGL(fn, dim3((unsigned)n_blocks), dim3(nw * 64), 0,
+  hipLaunchKernelGGL(fn, dim3((unsigned)n_blocks), dim3(waves * 64), 0,
                      static_cast<hipStream_t>(stream), p);
   if (hipGetLastError() != hipSuccess) return FA_EDEVICE;
   if (split) {  // merge the splits' row states into o and lse (same stream, so after the above)
