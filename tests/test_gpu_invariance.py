@@ -93,3 +93,30 @@ def test_layout_invariant(dtype):
     torch.cuda.synchronize()
     _same(o2, o1, "O BSHD")
     _same(l2, l1, "LSE BSHD")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_output_d_parts_equal_one_wave(d):
+    """Small fp32 calls whose automatic geometry is one-wave workgroups run with d / 32 waves per
+    32-row block, each computing the scores and weights and its own 32 output columns: the same
+    bits as the one-wave tiling, and the oracle's values."""
+    import oracle
+    from gpu_common import compare, host, scale_for
+    B, Hq, Hkv = 1, 4, 2
+    for Tq, Tk, flags in ((100, 100, dict(causal=True)), (65, 300, dict(causal=True, q_offset=235)),
+                          (1, 1000, dict(causal=True, q_offset=999)), (70, 129, dict(causal=False)),
+                          (50, 500, dict(causal=True, window=64, q_offset=400, sinks=True))):
+        q, k, v, z = make_inputs(f"inv-dparts/{d}/{Tq}/{Tk}", B, Hq, Hkv, Tq, Tk, d, "f32", sinks=True)
+        tq, tk, tv = dev(q), dev(k), dev(v)
+        kw = dict(flags)
+        kw["sinks"] = dev(z) if flags.get("sinks") else None
+        say("d-parts", d, Tq, Tk, sorted(flags))
+        o, lse = fa.forward(tq, tk, tv, scale=scale_for(d), **kw)
+        o1, l1 = fa.forward(tq, tk, tv, scale=scale_for(d), tiling=(32, 1), **kw)
+        torch.cuda.synchronize()
+        _same(o, o1, f"O d-parts {Tq}x{Tk}")
+        _same(lse, l1, f"LSE d-parts {Tq}x{Tk}")
+        o_ref, l_ref = oracle.attention(q, k, v, scale=scale_for(d), q_offset=flags.get("q_offset", 0),
+                                        causal=flags["causal"], window=flags.get("window", 0),
+                                        sinks=z if flags.get("sinks") else None)
+        compare(host(o), host(lse), o_ref, l_ref, "f32", f"d-parts {d} {Tq}x{Tk}")
