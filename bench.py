@@ -22,6 +22,8 @@ The same JSON line also reports
     8,192 tokens;
   * cpu_baseline: the fp64 oracle timed on the host cores over a bounded row sample of the
     headline workload;
+  * cpu_oracle_prefill: the same oracle over one layer of each prefill shape, on one host thread
+    and on all of them (context beside the pages' CPU prefill figures, not a target);
   * sclk_during_headline: the shader clock rocm-smi reports while the headline kernel runs;
   * inputs_sha256_16 (and mask_sha256_16 of the mask run): digests of the seeded host inputs,
     the same on every run and box.
@@ -416,6 +418,34 @@ def cpu_baseline(h, target_s=15.0):
                 seconds=round(dt, 2))
 
 
+def cpu_oracle_prefill():
+    """The fp64 oracle on the host, one layer of each prefill shape (16/8 heads, d 128, causal,
+    fp32 inputs; and the 1 x 128 x 64 single head), on one thread and on all host threads, to sit
+    beside the pages' CPU prefill figures.  28-layer figures are these times x 28."""
+    import oracle
+    import synth
+    cores = len(os.sched_getaffinity(0))
+    res = {"cores": cores}
+    for name, (Hq, Hkv, T, d, one_thread) in (("1x128_d64", (1, 1, 128, 64, True)),
+                                                ("511_f32_layer", (16, 8, 511, 128, True)),
+                                                ("2044_f32_layer", (16, 8, 2044, 128, False))):
+        q = synth.normal(synth.seed_of("cpu-prefill", name, "q"), (1, Hq, T, d), "f32")
+        k = synth.normal(synth.seed_of("cpu-prefill", name, "k"), (1, Hkv, T, d), "f32")
+        v = synth.normal(synth.seed_of("cpu-prefill", name, "v"), (1, Hkv, T, d), "f32")
+        scale = float(np.float32(1 / math.sqrt(d)))
+        row = {}
+        for label, thr in (("threads1_ms", 1), ("threads_all_ms", cores)):
+            if thr == 1 and not one_thread:
+                continue
+            t0 = time.perf_counter()
+            oracle.attention(q, k, v, scale=scale, causal=True, threads=thr)
+            row[label] = round((time.perf_counter() - t0) * 1e3, 2)
+        if Hq == 16:
+            row.update({key.replace("_ms", "_x28_ms"): round(ms * 28, 1) for key, ms in list(row.items())})
+        res[name] = row
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -498,6 +528,7 @@ def main():
         result["score_variants"] = bench_variants()
     if not args.no_cpu and not args.headline_only:
         result["cpu_baseline"] = cpu_baseline(h)
+        result["cpu_oracle_prefill"] = cpu_oracle_prefill()
     print(json.dumps(result), flush=True)
 
 
