@@ -14,6 +14,7 @@ The same JSON line also reports
     16 query / 8 KV heads, d 128: 511 tokens fp32, 2044 tokens fp32 and bf16; and
     prefill_ms_splitkv: the same through split-KV at the default split size (results within
     tolerance of the plain call, still invariant to query chunking at that split size);
+  * single_head_128: the 1 x 128 x 64 fp32 causal call (launch-latency bound);
   * extra workloads: the 32/8-head d 64 sliding-window (512) prefill with sinks, chunked
     (1000, 1000, 1000, 1096) and whole, the non-causal run with a broadcast additive mask, and
     decode (one query row, split-KV and unsplit) at 8 x 32/8 heads x 8,192 keys bf16 and at
@@ -205,6 +206,21 @@ def bench_prefill(T, dtype, layers=28, reps=5, split=False):
     if split:
         res["split_keys"] = int(sk)
     return res
+
+
+def bench_single_head(steps=20, warmup=5):
+    """The single-head case: B 1, H 1, Tq = Tk = 128, d 64, fp32, causal, with LSE (launch
+    latency bound: the call's duration, and the wall time per call back to back)."""
+    import torch
+    import flashattention_forward_flash_amd as fa
+    q, k, v = _inputs("c1", 1, 1, 1, 128, 128, 64, "f32")
+    out = torch.empty_like(q)
+    lse = torch.empty((1, 1, 128), dtype=torch.float32, device="cuda")
+    scale = float(np.float32(1 / math.sqrt(64)))
+    print("[bench] single head 1x128 d64 f32", file=sys.stderr, flush=True)
+    wall, ev = _timed(lambda: fa.forward(q, k, v, scale=scale, causal=True, out=out, lse=lse), steps, warmup)
+    return dict(event_us=round(ev * 1e3, 2), wall_us_per_call=round(wall * 1e3, 2),
+                tflops=round(4.0 * 64 * visible_pairs(128, 128) / (ev * 1e-3) / 1e12, 4))
 
 
 def bench_window_chunks(steps=10, warmup=3):
@@ -522,6 +538,7 @@ def main():
             "2044_f32_28L": bench_prefill(2044, "f32", split=True),
             "2044_bf16_28L": bench_prefill(2044, "bf16", split=True),
         }
+        result["single_head_128"] = bench_single_head()
         result["window_sinks_4096"] = bench_window_chunks()
         result["decode"] = bench_decode()
         result["varlen_batch"] = bench_varlen()
