@@ -139,6 +139,19 @@ def _check(status):
         raise FaError(status, fa_status_str(status))
 
 
+def _on_device(name, t, q):
+    """Raises FaError unless `t` (a tensor or None) lives on q's GPU: the library receives raw
+    device pointers, and a host pointer handed to a kernel would fault the GPU."""
+    if t is not None and (not t.is_cuda or t.device != q.device):
+        raise FaError(FA_EINVAL, f"{name} must be a GPU tensor on {q.device} (got {t.device})")
+
+
+def _check_out(out, q, shape):
+    """`out` must have q's dtype and the output shape, or the kernels would write out of bounds."""
+    if out.dtype != q.dtype or tuple(out.shape) != tuple(shape):
+        raise FaError(FA_EINVAL, f"out must be {q.dtype} {tuple(shape)} (got {out.dtype} {tuple(out.shape)})")
+
+
 def forward(q, k, v, *, scale=None, q_offset=0, causal=True, window=0, sinks=None, mask=None,
             out=None, lse=None, return_lse=True, tiling=None, stream=None, softcap=0.0, alibi_slopes=None):
     """O = softmax(scale * Q K^T + mask) V over torch tensors on the GPU.
@@ -174,6 +187,8 @@ def forward_splitkv(q, k, v, *, split_keys=0, workspace=None, scale=None, q_offs
     if workspace is None:
         nbytes = fa_splitkv_workspace_bytes(B, Hq, Tq, Tk, d, int(split_keys)) if split_keys > 0 else 0
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    if workspace.numel():
+        _on_device("workspace", workspace, q)
     ext = _variants(None, softcap, alibi_slopes, tiling, q)
     if ext is not None:
         ext.split_keys = int(split_keys)
@@ -207,6 +222,11 @@ def forward_paged(q, k_pool, v_pool, block_table, *, Tk=None, seqlens_k=None, sp
     if seqlens_k is not None and (seqlens_k.dtype != torch.int32 or tuple(seqlens_k.shape) != (B,)
                                   or not seqlens_k.is_contiguous()):
         raise FaError(FA_EINVAL, "seqlens_k must be a contiguous int32 [B] tensor")
+    if q.numel() and not q.is_cuda:
+        raise FaError(FA_EINVAL, "q must be a GPU tensor")
+    for name, t in (("block_table", block_table), ("seqlens_k", seqlens_k)):
+        if t is not None and t.numel():
+            _on_device(name, t, q)
     ext = fa_ext(block_table=block_table.data_ptr() if block_table.numel() else None,
                  block_table_stride=block_table.stride(0) if block_table.shape[0] > 1 else block_table.shape[1],
                  block_size=bs, num_blocks=nb,
@@ -275,10 +295,17 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.numel() and t.stride(-1) != 1:
             raise FaError(FA_EINVAL, f"{name}: the d axis must be contiguous")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.numel() and not t.is_cuda:
+            raise FaError(FA_EINVAL, f"{name} must be a GPU tensor")
+    for name, t in (("k", k), ("v", v), ("sinks", sinks), ("out", out), ("lse", lse), ("workspace", workspace)):
+        if t is not None and (t.numel() or name in ("sinks", "workspace")):
+            _on_device(name, t, q)
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
     if out is None:
         out = torch.empty((total_q, Hq, d), dtype=q.dtype, device=q.device)
+    _check_out(out, q, (total_q, Hq, d))
     if lse is None and return_lse:
         lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, total_q)
@@ -311,6 +338,7 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen
         if workspace is None:
             nbytes = fa_splitkv_workspace_bytes(B, Hq, Tq, Tk, d, int(split_keys)) if split_keys > 0 else 0
             workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+        _on_device("workspace", workspace, q)
         ext.split_keys = int(split_keys)
         ext.workspace = workspace.data_ptr()
         ext.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -373,10 +401,15 @@ def _forward(q, k, v, scale, q_offset, causal, window, sinks, mask, out, lse, re
             raise FaError(FA_EINVAL, f"{name}: the d axis must be contiguous")
         if t.numel() and not t.is_cuda:
             raise FaError(FA_EINVAL, f"{name} must be a GPU tensor")
+    for name, t in (("k", k), ("v", v), ("sinks", sinks), ("mask", mask), ("out", out), ("lse", lse),
+                    ("workspace", workspace)):
+        if t is not None and (t.numel() or name in ("sinks", "mask", "workspace")):
+            _on_device(name, t, q)
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
     if out is None:
         out = torch.empty((B, Hq, Tq, d), dtype=q.dtype, device=q.device)
+    _check_out(out, q, (B, Hq, Tq, d))
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
     st = fa_strides()

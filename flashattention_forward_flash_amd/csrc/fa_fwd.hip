@@ -167,11 +167,11 @@ struct SplitSpan {
   bool single;
   __device__ __forceinline__ SplitSpan(int64_t pos, const Params &p) {
     const int64_t lo = vis_lo(pos, p), hi = vis_hi(pos, p);  // both in [0, Tk]
-    const uint32_t kps = (uint32_t)p.split_tiles * 64u;
+    const int64_t kps = (int64_t)p.split_tiles * kBc;         // keys per split (the host caps it near Tk)
     s_lo = s_hi = 0;
     if (hi > lo) {
-      s_lo = (int)((uint32_t)lo / kps);
-      s_hi = (int)((uint32_t)(hi - 1) / kps) + 1;
+      s_lo = (int)(lo / kps);
+      s_hi = (int)((hi - 1) / kps) + 1;
     }
     single = s_hi == s_lo + 1 && (p.sinks == nullptr || s_lo == 0);
   }
@@ -915,8 +915,10 @@ struct Wave {
       for (int g = 0; g < 4; ++g) {
         const int d0 = (dpart * NOB + db) * 32 + 8 * g + 4 * half;  // registers 4g..4g+3 hold d0..d0+3
         float r4[4];
+        // (+ 0: a zero output is +0 whichever way it was reached, e.g. through a rescale by 0 of a
+        // negative accumulator, so that a row's bits never depend on which tiles its wave processed)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r4[e] = oacc[db][4 * g + e] * inv;
+        for (int e = 0; e < 4; ++e) r4[e] = oacc[db][4 * g + e] * inv + 0.f;
         if constexpr (BF16) {
           u32x2 pk = {pack_bf16x2(r4[0], r4[1]), pack_bf16x2(r4[2], r4[3])};
           *reinterpret_cast<u32x2 *>(orow + d0 * 2) = pk;
@@ -1280,19 +1282,21 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(Params p0) {
     }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) a[e] = a[e] * inv + 0.f;  // as in Wave::finish: zeros are +0
   unsigned char *orow = static_cast<unsigned char *>(p.o) +
                         ((int64_t)b * p.so_b + (int64_t)h * p.so_h + (p.q_start + i) * p.so_t) * (BF16 ? 2 : 4);
   if constexpr (BF16) {
     if constexpr (EPL == 2)
-      *reinterpret_cast<uint32_t *>(orow + 4 * lane) = pack_bf16x2(a[0] * inv, a[1] * inv);
+      *reinterpret_cast<uint32_t *>(orow + 4 * lane) = pack_bf16x2(a[0], a[1]);
     else
-      *reinterpret_cast<unsigned short *>(orow + 2 * lane) = __builtin_bit_cast(unsigned short, (__bf16)(a[0] * inv));
+      *reinterpret_cast<unsigned short *>(orow + 2 * lane) = __builtin_bit_cast(unsigned short, (__bf16)a[0]);
   } else {
     if constexpr (EPL == 2) {
-      const f32x2 v = {a[0] * inv, a[1] * inv};
+      const f32x2 v = {a[0], a[1]};
       *reinterpret_cast<f32x2 *>(orow + 8 * lane) = v;
     } else {
-      *reinterpret_cast<float *>(orow + 4 * lane) = a[0] * inv;
+      *reinterpret_cast<float *>(orow + 4 * lane) = a[0];
     }
   }
   if (p.lse && lane == 0)
@@ -1457,9 +1461,13 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
       return FA_EINVAL;
   }
   int64_t n_splits = 0;
+  int64_t split_eff = 0;  // keys per split as the kernels take it
   if (split) {
     if (split_keys < 0 || split_keys % 64 != 0) return FA_EINVAL;
-    n_splits = n_splits_of(Tk, split_keys);
+    // A split that holds every key is one split whatever its nominal size: cap it there, so the
+    // kernels' split arithmetic stays far inside 32 bits for any split_keys.
+    split_eff = std::min(split_keys, ceil_div(std::max(Tk, (int64_t)1), 64) * 64);
+    n_splits = n_splits_of(Tk, split_eff);
     if (rows_total > 0) {
       if (workspace == nullptr) return FA_EINVAL;
       if (n_splits > INT32_MAX / 4 || rows_total > INT64_MAX / (4 * (d + 2)) / n_splits) return FA_EUNSUPPORTED;
@@ -1528,7 +1536,7 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
                s.mask[1] % 4 == 0 && s.mask[2] % 4 == 0;
   p.tile_major = mask != nullptr && s.mask[0] == 0 && s.mask[1] == 0;
   p.n_splits = (int32_t)n_splits;
-  p.split_tiles = split ? (int32_t)std::min(split_keys / 64, (int64_t)INT32_MAX / 4) : 0;
+  p.split_tiles = split ? (int32_t)(split_eff / 64) : 0;
   p.ws_acc = split ? static_cast<float *>(workspace) : nullptr;
   p.ws_ml = split ? static_cast<float *>(workspace) + n_splits * rows_total * d : nullptr;
   p.block_table = x.block_table;

@@ -76,6 +76,9 @@ typedef struct {
  * The library allocates nothing and keeps no state: scratch is on-chip (LDS and
  * registers) and its size does not depend on Tk.  Calls on different streams may overlap.
  *
+ * A row with no visible key and no sink gets o = +0 (sign bit clear) and lse = -inf; every
+ * zero in o is written as +0.
+ *
  * Errors are returned synchronously, before any launch, and leave o and lse untouched:
  * FA_EINVAL, FA_ESHAPE and FA_EUNSUPPORTED as listed in fa_status.  B * Hq * Tq == 0 returns
  * FA_OK without a launch.  Tk == 0 is valid (k and v may then be NULL): every row gets
@@ -127,11 +130,13 @@ fa_status fa_fwd_tiled(const void *q, const void *k, const void *v, void *o, flo
  * which is the same o and lse as fa_fwd up to rounding (the pages: trading invariance for
  * parallelism).  The bits of a row depend on q_i, K, V, p_i, the flags, d, the dtype and
  * split_keys only: not on chunking, tiling, batch, strides or launch order.  With a single
- * split (split_keys >= Tk) the results equal fa_fwd's bit for bit (the sign of a zero aside).
+ * split (split_keys >= Tk) the results equal fa_fwd's bit for bit.  (Every entry point writes
+ * a zero output as +0.)
  *
  * Arguments as for fa_fwd_tiled, plus:
  *   split_keys       keys per split, a positive multiple of 64; 0 picks
- *                    fa_splitkv_default_keys(...).  Anything else returns FA_EINVAL.
+ *                    fa_splitkv_default_keys(...).  Anything else returns FA_EINVAL.  Any
+ *                    value >= Tk (up to INT64_MAX) is one split.
  *   workspace        device memory owned by the caller, 16-byte aligned, at least
  *                    fa_splitkv_workspace_bytes(B, Hq, Tq, Tk, d, split_keys) bytes (else
  *                    FA_EINVAL; misaligned: FA_EUNSUPPORTED).  Its contents on entry do not

@@ -12,7 +12,9 @@ and ALiBi score variants the candle page names; the C source header lists the re
 where the pages are silent.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` (worked example, closed
-forms, brute force in ``oracle/brute.py``, torch's fp64 SDPA, planted mistakes).
+forms, the 50-digit decimal brute force of ``tests/brute_decimal.py``, torch's fp64 SDPA,
+planted mistakes).  ``FA_ORACLE_LIB`` in the environment names another build of the same
+source to load instead (the sanitizer test runs the pins against an ASan/UBSan build).
 """
 import ctypes
 import os
@@ -26,7 +28,7 @@ _LIBS = {}
 
 
 def _load(path=None):
-    path = path or _build.LIB
+    path = path or os.environ.get("FA_ORACLE_LIB") or _build.LIB
     if path not in _LIBS:
         if path == _build.LIB and not os.path.exists(path):
             _build.build()

@@ -5,7 +5,8 @@ device copies, the fp64 oracle gets the host arrays.  The generator is splitmix6
 Box-Muller, written in ``gen.c`` (built with gcc on first use or by ``build()``).
 
 Seeds are derived from names: ``seed_of("c5", 0, "q")`` = first 8 bytes of
-SHA-256("c5/0/q"), so a tensor of any workload can be regenerated alone.
+SHA-256("c5/0/q"), so a tensor of any workload can be regenerated alone.  ``FA_SYNTH_LIB`` in
+the environment names another build of ``gen.c`` to load (the sanitizer test's).
 """
 import ctypes
 import hashlib
@@ -31,9 +32,10 @@ def build():
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB):
+        path = os.environ.get("FA_SYNTH_LIB") or LIB
+        if path == LIB and not os.path.exists(LIB):
             build()
-        lib = ctypes.CDLL(LIB)
+        lib = ctypes.CDLL(path)
         lib.synth_uniform_f64.argtypes = [ctypes.c_uint64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
         lib.synth_normal_f32.argtypes = [ctypes.c_uint64, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
                                          ctypes.c_float, ctypes.c_void_p]

@@ -51,18 +51,35 @@ def host(t):
 
 
 def bits(t):
-    """Raw bits of a GPU tensor as an integer numpy array, with -0.0 normalised to +0.0
-    (the one residue allowed between a row-invisible tile that was processed and one that
-    was skipped)."""
-    t = t.clone()
-    t[t == 0] = 0
+    """Raw bits of a GPU tensor as an integer numpy array (bitwise comparisons: the library
+    writes every zero output as +0, so no normalisation is needed)."""
     if t.dtype == torch.bfloat16:
-        return t.view(torch.int16).cpu().numpy()
-    return t.view(torch.int32).cpu().numpy()
+        return t.contiguous().view(torch.int16).cpu().numpy()
+    return t.contiguous().view(torch.int32).cpu().numpy()
+
+
+def bf16_round(x):
+    """fp64/fp32 values rounded to bf16 (nearest even) and widened back, for ulp comparisons."""
+    return synth.bf16_bits_to_f32(synth.to_bf16_bits(np.asarray(x, np.float32))).astype(np.float64)
+
+
+def bf16_ulps(got, ref):
+    """Distance in bf16 ulps between bf16 results `got` and RNE(ref), in units of the ulp at the
+    larger magnitude (8 significant bits: ulp(x) = 2^(floor(log2 |x|) - 7))."""
+    r = bf16_round(ref)
+    mag = np.maximum(np.abs(got), np.abs(r))
+    ulp = np.exp2(np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - 7)
+    return np.abs(got - r) / ulp
 
 
 def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what=""):
-    """Asserts parity with the oracle; returns (max |dO|, max |dLSE|)."""
+    """Asserts parity with the oracle; returns (max |dO|, max |dLSE|).
+
+    Rows with no visible key (oracle LSE -inf) must be exactly +0 (sign bit clear) with LSE -inf.
+    For bf16 outputs, elements with |o| >= 4 are held to 1 bf16 ulp of the rounded oracle value
+    instead of the absolute bound (half an ulp there is 2^-6 > 1.5e-2); the largest such
+    distance is reported.
+    """
     tol = TOL[dtype]
     o_gpu = np.asarray(o_gpu, np.float64)
     lse_gpu = np.asarray(lse_gpu, np.float64)
@@ -71,10 +88,20 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what=""):
     dead = lse_ref == -np.inf
     assert np.array_equal(lse_gpu == -np.inf, dead), f"{what}: -inf LSE rows differ"
     if dead.any():
-        assert np.all(o_gpu[dead] == 0), f"{what}: a row with no visible key is not zero"
-    do = float(np.max(np.abs(o_gpu - o_ref))) if o_ref.size else 0.0
+        od = o_gpu[dead]
+        assert np.all(od == 0) and not np.any(np.signbit(od)), f"{what}: a row with no visible key is not +0"
+    err = np.abs(o_gpu - o_ref)
+    big = np.zeros(o_ref.shape, bool)
+    ulps = 0.0
+    if dtype == "bf16":
+        big = np.abs(o_ref) >= 4
+        if big.any():
+            ulps = float(np.max(bf16_ulps(o_gpu[big], o_ref[big])))
+            assert ulps <= 1.0, f"{what}: {ulps} bf16 ulps at |o| >= 4"
+    do = float(np.max(err[~big])) if (~big).any() else 0.0
     dl = float(np.max(np.abs(lse_gpu[~dead] - lse_ref[~dead]))) if (~dead).any() else 0.0
-    print(f"[parity] {what} dtype={dtype} max|dO|={do:.3e} max|dLSE|={dl:.3e} tol={tol:g}", flush=True)
+    extra = f" |o|>=4: {int(big.sum())} elements, max {ulps:.2f} bf16 ulp" if big.any() else ""
+    print(f"[parity] {what} dtype={dtype} max|dO|={do:.3e} max|dLSE|={dl:.3e} tol={tol:g}{extra}", flush=True)
     assert do <= tol, f"{what}: max |dO| {do} > {tol}"
     assert dl <= tol, f"{what}: max |dLSE| {dl} > {tol}"
     return do, dl

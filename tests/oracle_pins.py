@@ -147,6 +147,34 @@ def pin_closed_form_q_zero_mask(attn):
         assert np.max(np.abs(lse[0, :, i] - math.log(n))) <= 1e-12
 
 
+def pin_closed_form_q_zero_mask_offset(attn):
+    """q = 0 with a 0/-inf additive mask on a chunk at q_offset > 0, causal, with and without a
+    window: o = mean of the values of keys that are both visible at the row's absolute position
+    p_i = q_offset + i and kept by mask row i of the call (the mask is indexed like q, by the
+    call's row; "Fused attention and softmax: fast and exact", "What is computed" gives the mask
+    as [qLen, kLen] of the call).  The mask array has rows past Tq, so that a reading by absolute
+    position stays inside it and gives a different answer."""
+    B, Hq, Hkv, Tq, Tk, d, qo = 1, 2, 1, 40, 70, 8, 17
+    q = np.zeros((B, Hq, Tq, d), np.float32)
+    v = synth.normal_f32(synth.seed_of("pin-q0mo", "v"), (B, Hkv, Tk, d))
+    k = synth.normal_f32(synth.seed_of("pin-q0mo", "k"), (B, Hkv, Tk, d))
+    big = synth.neg_inf_mask(synth.seed_of("pin-q0mo", "m"), (Tq + qo, Tk), 0.3)
+    big[7] = -np.inf  # a row that sees nothing
+    for window in (0, 9):
+        o, lse = attn(q, k, v, scale=0.3, q_offset=qo, causal=True, window=window, mask=big[:Tq][None, None])
+        for i in range(Tq):
+            lo, hi = _interval(qo + i, Tk, True, window)
+            keep = np.zeros(Tk, bool)
+            keep[lo:hi] = big[i, lo:hi] == 0
+            n = int(keep.sum())
+            if n == 0:
+                assert np.all(o[0, :, i] == 0) and np.all(lse[0, :, i] == -np.inf), (window, i)
+                continue
+            ref = v[0, 0, keep].astype(np.float64).mean(0)
+            assert np.max(np.abs(o[0, :, i] - ref)) <= 1e-12, (window, i)
+            assert np.max(np.abs(lse[0, :, i] - math.log(n))) <= 1e-12, (window, i)
+
+
 def pin_const_v(attn):
     """Every value row equal to c: o = c (1 - p_sink) for any scores, p_sink = e^{z - lse}."""
     B, Hq, Hkv, Tq, Tk, d = 2, 4, 2, 50, 90, 16
@@ -395,5 +423,5 @@ def pin_streamed_equals_materialised(attn):
 
 ALL_PINS = [pin_hand_example, pin_sinks, pin_no_visible_key, pin_closed_form_q_zero, pin_alibi_closed_form,
             pin_softcap_saturation,
-            pin_closed_form_q_zero_mask, pin_const_v, pin_single_visible_key, pin_mask_shift,
+            pin_closed_form_q_zero_mask, pin_closed_form_q_zero_mask_offset, pin_const_v, pin_single_visible_key, pin_mask_shift,
             pin_brute_force, pin_sdpa, pin_streamed_equals_materialised]

@@ -165,6 +165,17 @@ def test_splitkv_validation_errors(kw, want):
     assert _split_call(**kw) == want
 
 
+@pytest.mark.parametrize("split_keys", [2 ** 32, 2 ** 32 + 64, 2 ** 40])
+def test_splitkv_huge_split_is_one_split(split_keys):
+    """A split of 2^32 keys or more holds every key: the call needs the workspace of one split
+    (one byte less is refused) and goes on to the next checks (here a misaligned q, so that
+    nothing is launched)."""
+    one = fa.fa_splitkv_workspace_bytes(1, 4, 1, 1000, 64, 1024)
+    assert fa.fa_splitkv_workspace_bytes(1, 4, 1, 1000, 64, split_keys) == one
+    assert _split_call(split_keys=split_keys, ws_bytes=one - 1) == fa.FA_EINVAL
+    assert _split_call(split_keys=split_keys, ws_bytes=one, q=P + 8) == fa.FA_EUNSUPPORTED
+
+
 def test_splitkv_empty_work_returns_ok_without_launch():
     assert _split_call(Tq=0) == fa.FA_OK
     assert _split_call(B=0, ws=None, ws_bytes=0) == fa.FA_OK

@@ -91,7 +91,8 @@ def test_one_split_equals_unsplit(name, dtype):
     tm = None if m is None else dev(m)
     say("one split", name, dtype)
     o1, l1 = fa.forward(tq, tk, tv, sinks=tz, mask=tm, **kw)
-    for split in (64 * ((Tk + 63) // 64), 64 * ((Tk + 63) // 64) + 256):
+    # (2^32 and 2^32 + 64 keys per split: one split as well; the library caps a split at the keys)
+    for split in (64 * ((Tk + 63) // 64), 64 * ((Tk + 63) // 64) + 256, 2 ** 32, 2 ** 32 + 64):
         o2, l2 = fa.forward_splitkv(tq, tk, tv, split_keys=split, sinks=tz, mask=tm, **kw)
         torch.cuda.synchronize()
         assert np.array_equal(bits(o1), bits(o2)), f"O differs at split_keys {split}"
