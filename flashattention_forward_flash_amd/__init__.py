@@ -19,7 +19,8 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfa.so")
 
-FA_OK, FA_EINVAL, FA_ESHAPE, FA_EUNSUPPORTED, FA_EDEVICE = range(5)
+FA_OK, FA_EINVAL, FA_ESHAPE, FA_EUNSUPPORTED, FA_EDEVICE, FA_ESCRATCH = range(6)
+FA_NOALLOC_SCRATCH_BYTES = 32 << 20
 FA_F32, FA_BF16 = 0, 1
 
 
@@ -57,8 +58,8 @@ _lib = None
 _FWD_ARGS = [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int64] * 6 + [
     ctypes.c_float, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
     ctypes.POINTER(fa_strides), ctypes.c_int, ctypes.c_void_p]
-EXPORTED = ("fa_fwd", "fa_fwd_ext", "fa_fwd_splitkv", "fa_fwd_tiled", "fa_splitkv_default_keys",
-            "fa_splitkv_workspace_bytes", "fa_status_str")
+EXPORTED = ("fa_fwd", "fa_fwd_ext", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc", "fa_fwd_tiled",
+            "fa_splitkv_default_keys", "fa_splitkv_workspace_bytes", "fa_status_str")
 
 
 def load_library(path=None):
@@ -83,6 +84,8 @@ def load_library(path=None):
     lib.fa_fwd_splitkv.restype = ctypes.c_int
     lib.fa_fwd_splitkv.argtypes = _FWD_ARGS + [ctypes.POINTER(fa_tiling), ctypes.c_int64, ctypes.c_void_p,
                                                ctypes.c_size_t]
+    lib.fa_fwd_splitkv_noalloc.restype = ctypes.c_int
+    lib.fa_fwd_splitkv_noalloc.argtypes = _FWD_ARGS + [ctypes.POINTER(fa_tiling), ctypes.c_int64]
     lib.fa_fwd_ext.restype = ctypes.c_int
     lib.fa_fwd_ext.argtypes = _FWD_ARGS + [ctypes.POINTER(fa_ext)]
     lib.fa_splitkv_default_keys.restype = ctypes.c_int64
@@ -118,6 +121,14 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, caus
     return load_library().fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset,
                                           int(causal), window, sinks, mask, strides, dtype, stream, tiling,
                                           split_keys, workspace, workspace_bytes)
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, causal, window, sinks,
+                           mask, strides, dtype, stream, tiling, split_keys):
+    """fa_fwd_splitkv with the library's static scratch as the workspace (no allocation)."""
+    return load_library().fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset,
+                                                  int(causal), window, sinks, mask, strides, dtype, stream, tiling,
+                                                  split_keys)
 
 
 def fa_fwd_ext(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, causal, window, sinks, mask, strides,

@@ -48,6 +48,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "fa.h"
@@ -1387,11 +1388,12 @@ int64_t default_split_keys(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64
 int64_t n_splits_of(int64_t Tk, int64_t split_keys) { return std::max((int64_t)1, ceil_div(Tk, split_keys)); }
 
 // x: every optional feature, normalised (split_keys 0: no split, > 0: keys per split).
+// launch = false: every check, then FA_OK without launching.
 fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
                    int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d, float scale,
                    int64_t q_offset, int causal, int64_t window, const float *sinks,
                    const float *mask, const fa_strides *strides, fa_dtype dtype, void *stream,
-                   const fa_ext &x) {
+                   const fa_ext &x, bool launch = true) {
   const int64_t split_keys = x.split_keys;
   void *const workspace = x.workspace;
   const size_t workspace_bytes = x.workspace_bytes;
@@ -1574,6 +1576,7 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
     waves = (int)(d / 32);
     fn = d == 64 ? fa_fwd_kernel<false, 64, 2, 0, 2> : fa_fwd_kernel<false, 128, 4, 0, 4>;
   }
+  if (!launch) return FA_OK;
   (void)hipGetLastError();  // clear a stale error so the check below reports this launch
   hipLaunchKernelGGL(fn, dim3((unsigned)n_blocks), dim3(waves * 64), 0,
                      static_cast<hipStream_t>(stream), p);
@@ -1585,6 +1588,34 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
                        static_cast<hipStream_t>(stream), p);
     if (hipGetLastError() != hipSuccess) return FA_EDEVICE;
   }
+  return FA_OK;
+}
+
+// ---------------------------------------------------------------------------------------
+// Scratch for fa_fwd_splitkv_noalloc: the split-KV workspace of callers that cannot allocate
+// device memory.  Every GPU the library runs on holds its own copy of this array until the
+// process ends.  In host code its name is only a stand-in: the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and is the only form
+// handed to kernels.
+// ---------------------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(FA_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's address on the current device.
+fa_status scratch_of_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_EDEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return FA_EDEVICE;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
   return FA_OK;
 }
 
@@ -1649,6 +1680,39 @@ fa_status fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, f
                   mask, strides, dtype, stream, x);
 }
 
+fa_status fa_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                                  float scale, int64_t q_offset, int causal, int64_t window,
+                                  const float *sinks, const float *mask, const fa_strides *strides,
+                                  fa_dtype dtype, void *stream, const fa_tiling *tiling, int64_t split_keys) {
+  if (split_keys == 0) split_keys = default_split_keys(B, Hq, Hkv, Tq, Tk, q_offset, causal, window, dtype);
+  if (split_keys <= 0) return FA_EINVAL;
+  // the workspace this call needs (0 for arguments the checks below reject); its contents on
+  // entry do not matter, so nothing has to be cleared
+  const size_t need = fa_splitkv_workspace_bytes(B, Hq, Tq, Tk, d, split_keys);
+  if (need > kScratchBytes) return FA_ESCRATCH;
+  fa_ext x = {};
+  if (tiling) { x.rows_per_block = tiling->rows_per_block; x.heads_per_block = tiling->heads_per_block; }
+  x.split_keys = split_keys;
+  x.workspace_bytes = kScratchBytes;
+  // every argument check first (against a stand-in workspace address that nothing reads), so
+  // that errors do not depend on the device
+  x.workspace = reinterpret_cast<void *>(uintptr_t(256));
+  fa_status st = fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, causal, window, sinks,
+                          mask, strides, dtype, stream, x, false);
+  if (st != FA_OK) return st;
+  if (fa_splitkv_workspace_bytes(B, Hq, Tq, Tk, d, split_keys) == 0) {  // no rows: nothing to launch
+    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, causal, window, sinks, mask,
+                    strides, dtype, stream, x);
+  }
+  void *ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != FA_OK) return st;
+  x.workspace = ws;
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale, q_offset, causal, window, sinks,
+                  mask, strides, dtype, stream, x);
+}
+
 int64_t fa_splitkv_default_keys(int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk,
                                 int64_t q_offset, int causal, int64_t window, fa_dtype dtype) {
   return default_split_keys(B, Hq, Hkv, Tq, Tk, q_offset, causal, window, dtype);
@@ -1671,6 +1735,7 @@ const char *fa_status_str(fa_status s) {
     case FA_ESHAPE: return "invalid head shape (Hq must be a positive multiple of Hkv)";
     case FA_EUNSUPPORTED: return "unsupported (d must be 64 or 128; dtype fp32 or bf16; aligned tensors)";
     case FA_EDEVICE: return "device launch failed";
+    case FA_ESCRATCH: return "the call needs more workspace than the no-allocation scratch holds";
   }
   return "unknown status";
 }

@@ -37,7 +37,8 @@ typedef enum {
   FA_EINVAL = 1,       /* bad argument: negative size or q_offset, NULL tensor, bad stride, non-finite scale */
   FA_ESHAPE = 2,       /* head shapes: Hkv == 0 with Hq > 0, Hkv > Hq, or Hq % Hkv != 0 */
   FA_EUNSUPPORTED = 3, /* d not 64 or 128, unknown dtype, misaligned tensor, size beyond int32 */
-  FA_EDEVICE = 4       /* the HIP launch failed (no device, invalid stream, ...) */
+  FA_EDEVICE = 4,      /* the HIP launch failed (no device, invalid stream, ...) */
+  FA_ESCRATCH = 5      /* fa_fwd_splitkv_noalloc: the call needs more than FA_NOALLOC_SCRATCH_BYTES */
 } fa_status;
 
 typedef enum {
@@ -152,6 +153,28 @@ fa_status fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, f
                          const float *sinks, const float *mask, const fa_strides *strides,
                          fa_dtype dtype, void *stream, const fa_tiling *tiling, int64_t split_keys,
                          void *workspace, size_t workspace_bytes);
+
+/*
+ * fa_fwd_splitkv_noalloc -- fa_fwd_splitkv for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same call without the workspace arguments.  The workspace is a static device array inside
+ * the library, FA_NOALLOC_SCRATCH_BYTES bytes on each GPU it runs on, held until the process
+ * ends; the call allocates nothing and calls no allocating routine.  Results equal
+ * fa_fwd_splitkv's with the same split_keys bit for bit.
+ *
+ * Arguments as for fa_fwd_splitkv (split_keys 0: the default split).  A call whose workspace,
+ * fa_splitkv_workspace_bytes(B, Hq, Tq, Tk, d, split_keys), exceeds FA_NOALLOC_SCRATCH_BYTES
+ * returns FA_ESCRATCH before any launch; other errors as for fa_fwd_splitkv.  The array is
+ * shared by every call on a GPU and keeps the last call's contents (no call depends on them):
+ * calls that overlap in time on one GPU, on any streams, race on it and must not be issued.
+ * The stream must belong to the current device, whose array the call uses.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (32u << 20)
+fa_status fa_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                                 int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk, int64_t d,
+                                 float scale, int64_t q_offset, int causal, int64_t window,
+                                 const float *sinks, const float *mask, const fa_strides *strides,
+                                 fa_dtype dtype, void *stream, const fa_tiling *tiling, int64_t split_keys);
 
 /*
  * The split size fa_fwd_splitkv takes for split_keys = 0: a multiple of 64 (at least 256 for

@@ -49,7 +49,7 @@ def test_one_hip_runtime_whatever_the_import_order():
 
 
 def test_status_strings():
-    for s in range(5):
+    for s in range(6):
         assert fa.fa_status_str(s)
     assert fa.fa_status_str(99) == "unknown status"
 
@@ -174,6 +174,31 @@ def test_splitkv_huge_split_is_one_split(split_keys):
     assert fa.fa_splitkv_workspace_bytes(1, 4, 1, 1000, 64, split_keys) == one
     assert _split_call(split_keys=split_keys, ws_bytes=one - 1) == fa.FA_EINVAL
     assert _split_call(split_keys=split_keys, ws_bytes=one, q=P + 8) == fa.FA_EUNSUPPORTED
+
+
+def _noalloc_call(split_keys=256, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Hq=4, Hkv=2, Tq=1, Tk=1000, d=64, scale=0.125, q_offset=999,
+             causal=1, window=0, sinks=None, mask=None, strides=None, dtype=fa.FA_F32, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_splitkv_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                     a["Tq"], a["Tk"], a["d"], a["scale"], a["q_offset"], a["causal"],
+                                     a["window"], a["sinks"], a["mask"], a["strides"], a["dtype"], a["stream"],
+                                     None, split_keys)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(B=4096, Hq=64, Hkv=8, Tk=1 << 16, split_keys=1024), fa.FA_ESCRATCH),  # 64 splits x 2^18 rows
+    (dict(split_keys=100), fa.FA_EINVAL),
+    (dict(split_keys=-64), fa.FA_EINVAL),
+    (dict(Hq=6, Hkv=4), fa.FA_ESHAPE),
+    (dict(d=96), fa.FA_EUNSUPPORTED),
+    (dict(q=P + 8), fa.FA_EUNSUPPORTED),
+    (dict(Tq=0), fa.FA_OK),
+])
+def test_noalloc_errors_before_any_device_call(kw, want):
+    """The no-allocation entry point checks its arguments and the scratch size before it asks
+    for the scratch array's device address (so these hold without a GPU)."""
+    assert _noalloc_call(**kw) == want
 
 
 def test_splitkv_empty_work_returns_ok_without_launch():
