@@ -50,7 +50,8 @@ METRIC = "attention fwd TFLOP/s (causal-visible) + % MFMA peak; prefill ms @511/
 
 
 KERNEL_SRC = os.path.join(ROOT, "flashattention_forward_flash_amd", "csrc", "fa_fwd.hip")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fa_fwd_bf16_d128_causal_B8_H32_T8192_traffic.md")
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "fa_fwd_all_workloads.md")
+TRACE_SUMMARY = os.path.join(ROOT, "profiles", "fa_fwd_bf16_d128_causal_B8_H32_T8192.md")
 
 
 def kernel_source_hash():
@@ -58,18 +59,20 @@ def kernel_source_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the headline kernel from the committed counter summary, or None
-    when the summary is missing or was taken on a different kernel source."""
+def counter_traffic():
+    """{workload: figures} from the committed rocprofv3 counter summary (profiles/
+    fa_fwd_all_workloads.md: HBM bytes per step from FETCH_SIZE + WRITE_SIZE scaled by a plain
+    copy, the kernels' time per step), or {} when it is missing or was taken on a different
+    kernel source."""
     try:
-        text = open(TRAFFIC_SUMMARY).read()
+        text = open(PROFILE_SUMMARY).read()
     except OSError:
-        return None
-    src = re.search(r"kernel source sha256\[:16\]: ([0-9a-f]{16})", text)
-    val = re.search(r"traffic bytes per launch: (\d+)", text)
-    if not src or not val or src.group(1) != kernel_source_hash():
-        return None
-    return int(val.group(1))
+        return {}
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return {}
+    data = json.loads(m.group(1))
+    return data["workloads"] if data.get("kernel_source_sha256_16") == kernel_source_hash() else {}
 
 
 def copy_calibration(nbytes=1 << 30, reps=3):
@@ -462,6 +465,314 @@ def cpu_oracle_prefill():
     return res
 
 
+# ---- single workloads for the profiler (``--leg``): the same seeded inputs and calls as the legs
+# above, run `warmup + steps` times with nothing else on the GPU.  Each returns a callable that
+# performs one step and the step's algorithmic bytes and flops.
+def _leg_headline():
+    import torch
+    import flashattention_forward_flash_amd as fa
+    B, Hq, Hkv, T, d = 8, 32, 8, 8192, 128
+    q, k, v = _inputs("c5", B, Hq, Hkv, T, T, d, "bf16")
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+    scale = float(np.float32(1 / math.sqrt(d)))
+    nbytes = 2 * (q.numel() + k.numel() + v.numel() + out.numel()) + 4 * lse.numel()
+    return (lambda: fa.forward(q, k, v, scale=scale, causal=True, out=out, lse=lse)), nbytes, \
+        4.0 * d * B * Hq * visible_pairs(T, T)
+
+
+def _leg_mask():
+    import torch
+    import synth
+    import flashattention_forward_flash_amd as fa
+    B, Hq, Hkv, T, d = 8, 32, 8, 8192, 128
+    q, k, v = _inputs("c5", B, Hq, Hkv, T, T, d, "bf16")
+    m = synth.neg_inf_mask(synth.seed_of("c5", "mask"), (T, T), 0.1)
+    for r in (0, 1, 63, 64, 65, 127, 128, 1023, 1024, 2047, 4095, 4096, 6000, 8127, 8128, 8191):
+        m[r] = -np.inf
+    mask = torch.from_numpy(m).cuda()
+    out = torch.empty_like(q)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    nbytes = 2 * (q.numel() + k.numel() + v.numel() + out.numel()) + 4 * mask.numel()
+    return (lambda: fa.forward(q, k, v, scale=scale, causal=False, mask=mask, out=out, return_lse=False)), \
+        nbytes, 4.0 * d * B * Hq * T * T
+
+
+def _leg_prefill(T, dtype):
+    import torch
+    import flashattention_forward_flash_amd as fa
+    Hq, Hkv, d, layers = 16, 8, 128, 28
+    per_layer = [_inputs(f"prefill{T}/{dtype}/{layer}", 1, Hq, Hkv, T, T, d, dtype, layout="bshd")
+                 for layer in range(layers)]
+    outs = [torch.empty((1, T, Hq, d), dtype=per_layer[0][0].dtype, device="cuda").transpose(1, 2)
+            for _ in range(layers)]
+    scale = float(np.float32(1 / math.sqrt(d)))
+    es = 4 if dtype == "f32" else 2
+
+    def run_all():
+        for (q, k, v), o in zip(per_layer, outs):
+            fa.forward(q, k, v, scale=scale, causal=True, out=o, return_lse=False)
+
+    nbytes = layers * es * (2 * T * Hq * d + 2 * T * Hkv * d)
+    return run_all, nbytes, 4.0 * d * Hq * visible_pairs(T, T) * layers
+
+
+def _leg_single_head():
+    import torch
+    import flashattention_forward_flash_amd as fa
+    q, k, v = _inputs("c1", 1, 1, 1, 128, 128, 64, "f32")
+    out = torch.empty_like(q)
+    lse = torch.empty((1, 1, 128), dtype=torch.float32, device="cuda")
+    scale = float(np.float32(1 / math.sqrt(64)))
+    return (lambda: fa.forward(q, k, v, scale=scale, causal=True, out=out, lse=lse)), \
+        4 * (4 * 128 * 64) + 4 * 128, 4.0 * 64 * visible_pairs(128, 128)
+
+
+def _leg_window(chunked):
+    import torch
+    import synth
+    import flashattention_forward_flash_amd as fa
+    Hq, Hkv, T, d = 32, 8, 4096, 64
+    q, k, v = _inputs("c4", 1, Hq, Hkv, T, T, d, "f32")
+    z = torch.from_numpy(synth.normal_f32(synth.seed_of("c4", "z"), (Hq,))).cuda()
+    scale = float(np.float32(1 / math.sqrt(d)))
+    out = torch.empty_like(q)
+    lse = torch.empty((1, Hq, T), dtype=torch.float32, device="cuda")
+    chunks = [(0, 1000), (1000, 1000), (2000, 1000), (3000, 1096)] if chunked else [(0, T)]
+
+    def run():
+        for s0, n in chunks:
+            fa.forward(q[:, :, s0:s0 + n], k, v, scale=scale, q_offset=s0, causal=True, window=512, sinks=z,
+                       out=out[:, :, s0:s0 + n], lse=lse[:, :, s0:s0 + n])
+
+    nbytes = 4 * (q.numel() + k.numel() + v.numel() + out.numel() + lse.numel() + Hq)
+    return run, nbytes, 4.0 * d * Hq * visible_pairs(T, T, 0, True, 512)
+
+
+def _leg_decode(B, Hq, Hkv, Tk, d, dtype):
+    import torch
+    import flashattention_forward_flash_amd as fa
+    name = {8: "8x32x8192_bf16_d128"}.get(B, f"1x9x{Tk}_f32_d64")
+    q, k, v = _inputs(f"decode/{name}", B, Hq, Hkv, 1, Tk, d, dtype)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, 1), dtype=torch.float32, device="cuda")
+    split = fa.fa_splitkv_default_keys(B, Hq, Hkv, 1, Tk, Tk - 1, True, 0, fa.FA_BF16 if dtype == "bf16" else fa.FA_F32)
+    ws = torch.empty(fa.fa_splitkv_workspace_bytes(B, Hq, 1, Tk, d, split), dtype=torch.uint8, device="cuda")
+    es = q.element_size()
+    nbytes = es * (q.numel() + k.numel() + v.numel() + out.numel()) + 4 * lse.numel()
+    return (lambda: fa.forward_splitkv(q, k, v, split_keys=split, workspace=ws, scale=scale, q_offset=Tk - 1,
+                                       causal=True, out=out, lse=lse)), nbytes, 4.0 * d * B * Hq * Tk
+
+
+LEGS = {
+    "headline": _leg_headline,
+    "mask": _leg_mask,
+    "prefill511_f32": lambda: _leg_prefill(511, "f32"),
+    "prefill2044_f32": lambda: _leg_prefill(2044, "f32"),
+    "prefill2044_bf16": lambda: _leg_prefill(2044, "bf16"),
+    "single_head": _leg_single_head,
+    "window_sinks": lambda: _leg_window(False),
+    "window_sinks_chunked": lambda: _leg_window(True),
+    "decode_bf16": lambda: _leg_decode(8, 32, 8, 8192, 128, "bf16"),
+    "decode_f32_1024": lambda: _leg_decode(1, 9, 3, 1024, 64, "f32"),
+    "decode_f32_4096": lambda: _leg_decode(1, 9, 3, 4096, 64, "f32"),
+}
+
+
+def run_leg(name, steps, warmup):
+    """One workload, `warmup + steps` steps back to back (for rocprofv3)."""
+    import torch
+    import flashattention_forward_flash_amd as fa
+    fa.load_library()
+    fn, nbytes, flops = LEGS[name]()
+    for _ in range(warmup + steps):
+        fn()
+    torch.cuda.synchronize()
+    print(json.dumps({"leg": name, "steps": steps, "warmup": warmup, "algorithmic_bytes": nbytes,
+                      "flops": flops}), flush=True)
+
+
+SQ_SUMMARY = os.path.join(ROOT, "profiles", "fa_fwd_bf16_d128_causal_B8_H32_T8192_sq.md")
+SQ_COUNTERS = (("SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+                "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM"),
+               ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_ANY",
+                "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY"),
+               ("SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_VALU_TRANS_F32", "SQ_BUSY_CU_CYCLES"))
+
+
+def profile_commands(leg, steps=10, warmup=2):
+    """The rocprofv3 commands whose CSV output write_profile_summaries() reads (DIR = <repo>/gpurun_out/prof)."""
+    b = f"python3 <repo>/bench.py --leg {leg} --steps {steps} --warmup {warmup}"
+    return [f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR/{leg}_trace -o run -- {b}",
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/{leg}_FETCH_SIZE -o run -- {b}",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/{leg}_WRITE_SIZE -o run -- {b}"]
+
+
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name):
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0]
+
+
+def _write_trace_summary(d, leg, src):
+    """The headline's kernel trace: every call's duration, the average after the warm-up steps
+    (what bench.py's per-launch timing compares to) and rocprofv3's own --stats line."""
+    meta = json.loads(open(os.path.join(d, f"{leg}_trace", "leg.json")).read().strip().splitlines()[-1])
+    trace = sorted((r for r in _csv_rows(os.path.join(d, f"{leg}_trace", "run_kernel_trace.csv"))
+                    if "fa_fwd_kernel" in r["Kernel_Name"]), key=lambda r: int(r["Start_Timestamp"]))
+    us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace]
+    timed = us[meta["warmup"]:]
+    stats = [r for r in _csv_rows(os.path.join(d, f"{leg}_trace", "run_kernel_stats.csv"))
+             if "fa_fwd_kernel" in r["Name"]]
+    flops = meta["flops"]
+    lines = ["# fa_fwd kernel, bf16, d = 128, causal, B = 8, Hq = 32, Hkv = 8, Tq = Tk = 8192", "",
+             "Kernel trace of the headline workload (one call = one step of `bench.py`).", "",
+             "Command (repository root on one MI355X, `cd /tmp && export TMPDIR=/tmp` first; DIR =",
+             "`<repo>/gpurun_out/prof`):", "", "```",
+             f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR/{leg}_trace -o run -- python3 "
+             f"<repo>/bench.py --leg {leg} --steps {meta['steps']} --warmup {meta['warmup']}",
+             "python3 bench.py --profile-summary DIR   # writes this file", "```", "",
+             f"kernel source sha256[:16]: {src}", "",
+             "| kernel | calls | average us (all) | average us (after the warm-up call) | min us | max us |",
+             "|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(np.mean(timed)):.1f} | {float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    lines += ["", "Per call (us): " + ", ".join(f"{u:.1f}" for u in us), "",
+              f"The first {meta['warmup']} call(s) are the warm-up.  Causal-visible work per call: {flops:.4e} flop; "
+              f"the average after the warm-up, {np.mean(timed):.1f} us, is {flops / (np.mean(timed) * 1e-6) / 1e12:.0f} "
+              f"TFLOP/s under the profiler ({flops / (np.mean(timed) * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.3f} of the "
+              f"{PEAK_BF16_TFLOPS} TFLOP/s dense bf16 peak).", ""]
+    with open(TRACE_SUMMARY, "w") as f:
+        f.write("\n".join(lines))
+
+
+def write_profile_summaries(d):
+    """Turns rocprofv3 CSV output under `d` into the profiles/ summaries: per workload, the kernels'
+    average time per step after the warm-up steps (kernel trace), and the HBM bytes per step from
+    FETCH_SIZE and WRITE_SIZE, each scaled by what the same counter reads for a plain 1 GiB copy;
+    for the headline workload also the SQ counters.  Expects DIR/<leg>_trace/, DIR/<leg>_FETCH_SIZE/,
+    DIR/<leg>_WRITE_SIZE/ (each with leg.json, the leg's own output line), DIR/copy_FETCH_SIZE/,
+    DIR/copy_WRITE_SIZE/ and DIR/headline_sq<n>/."""
+    def counter_kib(sub):
+        rows = _csv_rows(os.path.join(d, sub, "run_counter_collection.csv"))
+        per = {}  # (dispatch, kernel) -> counter -> value summed over the rows (instances) of the dispatch
+        for r in rows:
+            c = per.setdefault((int(r["Dispatch_Id"]), r["Kernel_Name"]), {})
+            c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        return per
+
+    scale = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        vals = [v[c] for (_, name), v in counter_kib(f"copy_{c}").items() if "copy" in name.lower()]
+        scale[c] = (1 << 20) / float(np.mean(vals))  # KiB the counter reads for 1 GiB moved
+    legs = sorted({n[:-len("_trace")] for n in os.listdir(d) if n.endswith("_trace")})
+    src = kernel_source_hash()
+    lines = ["# HBM traffic and kernel time of every bench workload",
+             "",
+             "Per workload (one step = what `bench.py` times for it: one call, or the 28 calls of a",
+             "28-layer prefill, or the 4 calls of the chunked window run; decode runs split-KV: the",
+             "streaming kernel and the merge): the kernels' time per step averaged over the steps after",
+             "the warm-up (kernel trace), and the HBM bytes per step from the FETCH_SIZE and WRITE_SIZE",
+             "counters (KiB per dispatch, each pass a run of its own), scaled by what the same counter",
+             "reads for a plain 1 GiB device copy: FETCH_SIZE x %.4f, WRITE_SIZE x %.4f." % (
+                 scale["FETCH_SIZE"], scale["WRITE_SIZE"]),
+             "Algorithmic bytes read Q, K, V (and the mask, sinks) once and write O (and LSE) once.",
+             "",
+             "Commands (repository root on one MI355X, `cd /tmp && export TMPDIR=/tmp` first; DIR is",
+             "`<repo>/gpurun_out/prof`; the calibration copy is `python3 <repo>/bench.py --copy-calibration`",
+             "under the same two counter passes, into DIR/copy_FETCH_SIZE and DIR/copy_WRITE_SIZE); for",
+             "each workload LEG below:",
+             "",
+             "```"] + profile_commands("LEG") + [
+             "python3 bench.py --profile-summary DIR   # writes this file",
+             "```",
+             "",
+             f"kernel source sha256[:16]: {src}",
+             "",
+             "| workload | kernels | us per step | TFLOP/s | algorithmic bytes | counter bytes (read + write) | read / algorithmic read | GB/s (counters) |",
+             "|---|---|---|---|---|---|---|---|"]
+    machine = {}
+    for leg in legs:
+        meta = json.loads(open(os.path.join(d, f"{leg}_trace", "leg.json")).read().strip().splitlines()[-1])
+        steps, warmup = meta["steps"], meta["warmup"]
+        # the library's kernels only (torch's setup copies of the inputs are not part of a step)
+        trace = [r for r in _csv_rows(os.path.join(d, f"{leg}_trace", "run_kernel_trace.csv"))
+                 if "fa_fwd_kernel" in r["Kernel_Name"] or "fa_merge_kernel" in r["Kernel_Name"]]
+        trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+        per_step = len(trace) // (steps + warmup)
+        timed = trace[warmup * per_step:]
+        us = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in timed) / 1e3 / steps
+        names = sorted({_short(r["Kernel_Name"]) for r in trace})
+        byts = {}
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            per = {key: v for key, v in counter_kib(f"{leg}_{c}").items()
+                   if "fa_fwd_kernel" in key[1] or "fa_merge_kernel" in key[1]}
+            ids = sorted(per)[warmup * per_step:]
+            byts[c] = sum(per[i][c] for i in ids) * 1024 * scale[c] / steps
+        total = byts["FETCH_SIZE"] + byts["WRITE_SIZE"]
+        algo = meta["algorithmic_bytes"]
+        gbs = total / (us * 1e-6) / 1e9
+        tfl = meta["flops"] / (us * 1e-6) / 1e12
+        # the algorithmic reads: every input once (the bench's count minus the outputs)
+        machine[leg] = dict(us_per_step=round(us, 2), counter_bytes_per_step=int(total),
+                            read_bytes_per_step=int(byts["FETCH_SIZE"]), write_bytes_per_step=int(byts["WRITE_SIZE"]),
+                            algorithmic_bytes=algo, GBs=round(gbs, 1), kernels=names,
+                            dispatches_per_step=per_step)
+        lines.append(f"| {leg} | {', '.join('`' + n + '`' for n in names)} ({per_step} per step) | {us:.1f} | "
+                     f"{tfl:.2f} | {algo:,} | {int(total):,} | {byts['FETCH_SIZE'] / max(1, algo - byts['WRITE_SIZE']):.2f} "
+                     f"| {gbs:.1f} |")
+    lines += ["", "Machine-readable (bench.py reports these while the kernel source hash matches):", "",
+              "```json", json.dumps({"kernel_source_sha256_16": src, "workloads": machine}, indent=1), "```", ""]
+    with open(PROFILE_SUMMARY, "w") as f:
+        f.write("\n".join(lines))
+    _write_trace_summary(d, "headline", src)
+    # SQ counters of the headline kernel
+    sq = {}
+    for n in range(len(SQ_COUNTERS)):
+        sub = os.path.join(d, f"headline_sq{n}")
+        if not os.path.isdir(sub):
+            continue
+        rows = _csv_rows(os.path.join(sub, "run_counter_collection.csv"))
+        meta = json.loads(open(os.path.join(sub, "leg.json")).read().strip().splitlines()[-1])
+        ids = set(sorted({int(r["Dispatch_Id"]) for r in rows})[meta["warmup"]:])
+        per = {}
+        for r in rows:
+            if int(r["Dispatch_Id"]) in ids:
+                key = (int(r["Dispatch_Id"]), r["Counter_Name"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        for (_, name), val in per.items():
+            sq.setdefault(name, []).append(val)
+    if sq:
+        mean = {k: float(np.mean(v)) for k, v in sq.items()}
+        waves = mean.get("SQ_WAVES", 1.0)
+        tiles = 8 * 32 * 8192 // 32 * (8192 // 64 + 1) / 2  # wave-tiles per call (32-row waves, causal)
+        cmd = [f"rocprofv3 --pmc {' '.join(g)} --output-format csv -d DIR/headline_sq{n} -o run -- "
+               f"python3 <repo>/bench.py --leg headline --steps 3 --warmup 1" for n, g in enumerate(SQ_COUNTERS)]
+        out = ["# SQ counters of the headline kernel (bf16, d 128, causal, B 8, Hq 32, Hkv 8, T 8192)", "",
+               "Per dispatch after the warm-up, summed over the device (one rocprofv3 pass per group of",
+               "at most 8 SQ counters).  Commands (`cd /tmp && export TMPDIR=/tmp` first, DIR as in",
+               "`fa_fwd_all_workloads.md`):", "", "```"] + cmd + ["```", "",
+               f"kernel source sha256[:16]: {src}", "",
+               "| counter | per dispatch | per wave | per wave-tile (32 rows x 64 keys) |", "|---|---|---|---|"]
+        for k in sorted(mean):
+            out.append(f"| {k} | {mean[k]:.4g} | {mean[k] / waves:.4g} | {mean[k] / tiles:.4g} |")
+        busy = mean.get("SQ_BUSY_CYCLES")
+        mfma = mean.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        if busy and mfma:
+            # SQ_BUSY_CYCLES counts per shader engine (32 instances); SQ_VALU_MFMA_BUSY_CYCLES per SIMD
+            out += ["", f"MFMA-busy fraction: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x SQ_BUSY_CYCLES / 32) = "
+                        f"{mfma / (1024 * busy / 32):.3f}"]
+        with open(SQ_SUMMARY, "w") as f:
+            f.write("\n".join(out) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -471,7 +782,13 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (reference for the memory counters)")
+    ap.add_argument("--leg", choices=sorted(LEGS), help="only run this workload warmup + steps times (profiling)")
+    ap.add_argument("--profile-summary", metavar="DIR",
+                    help="write the profiles/ summaries from the rocprofv3 CSV output under DIR (no GPU)")
     args = ap.parse_args()
+    if args.profile_summary:
+        write_profile_summaries(args.profile_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only (the pass would shard over (b, head group) or query "
               "tiles with no exchange between GPUs; runs on several GPUs are not supported). Use --gpus 1.",
@@ -480,11 +797,15 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.leg:
+        run_leg(args.leg, args.steps, args.warmup)
+        return
     import torch
     import flashattention_forward_flash_amd as fa
     fa.load_library()
     torch.cuda.init()
 
+    counters = counter_traffic()
     h = bench_headline(args.steps, args.warmup)
     tflops = h["flops"] / (h["wall_ms"] * 1e-3) / 1e12
     achieved = h["flops"] / (h["event_ms"] * 1e-3) / 1e12
@@ -507,17 +828,13 @@ def main():
         "frac_mfma_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic()},
+                     "traffic": counters.get("headline", {}).get("counter_bytes_per_step")},
         "kernel_source_sha256_16": kernel_source_hash(),
         "kernel_ms": round(h["event_ms"], 4),
         "algorithmic_bytes": h["bytes"],
         "inputs_sha256_16": h["digests"],
     }
-    traffic = result["roofline"]["traffic"]
-    if traffic:  # HBM bytes per launch from the rocprofv3 counters, over this run's launch time
-        gbs = traffic / (h["event_ms"] * 1e-3) / 1e9
-        result["hbm_from_counters"] = {"bytes_per_launch": traffic, "GBs": round(gbs, 1),
-                                       "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    leg_ms = {"headline": h["event_ms"]}
     clk = sample_sclk(h)
     result["sclk_during_headline"] = clk
     if clk:  # the published peak assumes 2.4 GHz; the same fraction at the clock the box ran at
@@ -543,6 +860,23 @@ def main():
         result["decode"] = bench_decode()
         result["varlen_batch"] = bench_varlen()
         result["score_variants"] = bench_variants()
+    if not args.headline_only:
+        pf, dec = result["prefill_ms"], result["decode"]
+        leg_ms.update({"mask": result["mask_run"]["ms"], "prefill511_f32": pf["511_f32_28L"]["ms"],
+                       "prefill2044_f32": pf["2044_f32_28L"]["ms"], "prefill2044_bf16": pf["2044_bf16_28L"]["ms"],
+                       "single_head": result["single_head_128"]["event_us"] / 1e3,
+                       "window_sinks": result["window_sinks_4096"]["ms"],
+                       "window_sinks_chunked": result["window_sinks_4096"]["chunked_ms"],
+                       "decode_bf16": dec["8x32x8192_bf16_d128"]["splitkv_us"] / 1e3,
+                       "decode_f32_1024": dec["1x9x1024_f32_d64"]["splitkv_us"] / 1e3,
+                       "decode_f32_4096": dec["1x9x4096_f32_d64"]["splitkv_us"] / 1e3})
+    if counters:
+        # HBM bytes per step from the committed rocprofv3 counters, over this run's time per step
+        result["hbm_from_counters"] = {
+            leg: {"bytes_per_step": c["counter_bytes_per_step"], "algorithmic_bytes": c["algorithmic_bytes"],
+                  "GBs": round(c["counter_bytes_per_step"] / (leg_ms[leg] * 1e-3) / 1e9, 1),
+                  "frac_hbm_peak": round(c["counter_bytes_per_step"] / (leg_ms[leg] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            for leg, c in counters.items() if leg in leg_ms}
     if not args.no_cpu and not args.headline_only:
         result["cpu_baseline"] = cpu_baseline(h)
         result["cpu_oracle_prefill"] = cpu_oracle_prefill()

@@ -69,6 +69,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.f;  // base-2 headroom before the running maximum is moved
 constexpr float kLazyW = 256.f;  // 2^kLazy
+#ifndef FA_MASK_SLICE_BLOCK
+#define FA_MASK_SLICE_BLOCK 4  // work order of a broadcast mask: slices per block (see Work)
+#endif
 #ifndef FA_QK_LOOKAHEAD
 #define FA_QK_LOOKAHEAD 2  // QK steps the K operand reads run ahead of the MFMAs (at most 6)
 #endif
@@ -91,7 +94,7 @@ struct Params {
   int32_t n_blocks;
   int32_t causal;
   int32_t mask_vec;        // mask rows contiguous and 16-byte aligned: read 4 entries at a time
-  int32_t tile_major;      // order work query-tile-major (a mask shared by every (b, h))
+  int32_t tile_major;      // > 0: blocked order for a mask shared by every (b, h), this many slices per block
   int32_t mask_lds;        // MODE 1: each tile's 32 x 64 mask block is staged in LDS (MaskCopier)
   float scale_log2;        // scale * log2(e)
   float scale;             // scale (MODE 1 scores are scale q.k + mask, in natural units)
@@ -337,13 +340,21 @@ struct Work {
     int rest = w / p.n_head_groups;
     int rti;
     split = 0;
-    if (p.tile_major) {  // (row tile, split, b, kv head, head group): neighbours share mask rows
+    if (p.tile_major) {
+      // A mask shared by every (b, h): work comes in blocks of tile_major slices (a slice = one
+      // (split, b, kv head, head group)) by every row tile, slice fastest, so that the
+      // workgroups an XCD runs together share both mask rows (same row tile) and K/V tiles
+      // (same slice).  `hg` above is the slice's head group.
+      const int sb = p.tile_major;
+      const int s_in = w / p.n_head_groups % sb;
+      rest = w / p.n_head_groups / sb;
+      rti = rest % p.n_row_tiles;
+      rest = (rest / p.n_row_tiles) * sb + s_in;  // the slice, without its head group
       kvh = rest % p.Hkv;
       rest /= p.Hkv;
       b = rest % p.B;
       rest /= p.B;
-      if (p.n_splits > 0) { split = rest % p.n_splits; rest /= p.n_splits; }
-      rti = rest;
+      if (p.n_splits > 0) split = rest;
     } else {             // (b, kv head, split, row tile, head group): neighbours share K and V
       rti = rest % p.n_row_tiles;
       rest /= p.n_row_tiles;
@@ -1037,16 +1048,18 @@ struct Copier {
 };
 
 // ---------------------------------------------------------------------------------------
-// Mask tiles through LDS (MODE 1 when the workgroup's 32 rows share their mask rows across its
-// heads, mask rows contiguous and 16-byte aligned): the 32 x 64 fp32 block of tile t, row-major
+// Mask tiles through LDS (MODE 1 when the workgroup's MR rows share their mask rows across its
+// heads, mask rows contiguous and 16-byte aligned): the MR x 64 fp32 block of tile t, row-major
 // 256 bytes per row with the 16-byte chunks of row r stored at chunk ^ (r % 16), is copied
-// like K and V (8 blocks of 4 rows, split over the waves).  Rows past Tq and entries past the
+// like K and V (MR / 4 blocks of 4 rows, split over the waves).  MR is 64 for 8-wave
+// workgroups (two 32-row halves of 4 heads each), else 32.  Rows past Tq and entries past the
 // mask's last valid entry read as zeros; other entries past Tk belong to keys that the select
 // removes.
 // ---------------------------------------------------------------------------------------
 template <int NW>
 struct MaskCopier {
-  static constexpr int MPW = 8 / NW;  // 1 KiB blocks each wave copies per tile
+  static constexpr int MR = NW == 8 ? 64 : 32;  // staged rows
+  static constexpr int MPW = MR / 4 / NW;       // 1 KiB blocks each wave copies per tile
   const unsigned char *base;          // mask row row0 of the workgroup, key 0
   int64_t bytes_to_end;               // from base to the end of entry (Tq - 1, Tk - 1)
   int wid;
@@ -1095,7 +1108,7 @@ fa_fwd_kernel(Params p0) {
   __shared__ __attribute__((aligned(1024))) unsigned char k1[L::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char v0[L::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char v1[L::TILE_BYTES];
-  constexpr int MBYTES = MODE == 1 ? 32 * 256 : 16;  // staged mask blocks (MODE 1)
+  constexpr int MBYTES = MODE == 1 ? MaskCopier<NW>::MR * 256 : 16;  // staged mask blocks (MODE 1)
   __shared__ __attribute__((aligned(1024))) unsigned char m0[MBYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char m1[MBYTES];
 
@@ -1502,10 +1515,16 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   const bool auto_geom = rows_pb == 0 && !split;
   if (rows_pb == 0) {
     if (split) split_tiling(group, Tq, &rows_pb, &heads_pb);
-    else auto_tiling(B, Hkv, group, Tq,
-                     dtype == FA_BF16 && d == 128 && mask == nullptr && !(x.softcap > 0.f) && !x.alibi_slopes &&
-                         scale > 0.f,
-                     &rows_pb, &heads_pb);
+    else {
+      // a mask shared by every head: 8 waves only where they make 64-row workgroups of 4 heads,
+      // whose mask block is staged in LDS
+      const bool mask_eight = mask != nullptr && s.mask[1] == 0 && s.mask[3] == 1 && group % 4 == 0 &&
+                              group % 8 != 0;
+      auto_tiling(B, Hkv, group, Tq,
+                  dtype == FA_BF16 && d == 128 && (mask == nullptr || mask_eight) && !(x.softcap > 0.f) &&
+                      !x.alibi_slopes && scale > 0.f,
+                  &rows_pb, &heads_pb);
+    }
   }
   const int nw = (int)((int64_t)rows_pb * heads_pb / 32);
   const int64_t n_row_tiles = (Tq + rows_pb - 1) / rows_pb;
@@ -1536,7 +1555,16 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   p.scale = scale;
   p.mask_vec = mask != nullptr && s.mask[3] == 1 && aligned(mask, 16) && s.mask[0] % 4 == 0 &&
                s.mask[1] % 4 == 0 && s.mask[2] % 4 == 0;
-  p.tile_major = mask != nullptr && s.mask[0] == 0 && s.mask[1] == 0;
+  p.tile_major = 0;
+  if (mask != nullptr && s.mask[0] == 0 && s.mask[1] == 0) {
+    // slices (without head groups) per block: the largest divisor of their count up to
+    // FA_MASK_SLICE_BLOCK, which balances mask re-reads against K/V re-reads
+    const int64_t n_sl = B * Hkv * (split ? n_splits : 1);
+    int sb = 1;
+    for (int c = FA_MASK_SLICE_BLOCK; c >= 1; --c)
+      if (n_sl % c == 0) { sb = c; break; }
+    p.tile_major = sb;
+  }
   p.n_splits = (int32_t)n_splits;
   p.split_tiles = split ? (int32_t)(split_eff / 64) : 0;
   p.ws_acc = split ? static_cast<float *>(workspace) : nullptr;
@@ -1562,9 +1590,11 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   // 4 (ALiBi alone).
   const int mode = (x.softcap > 0.f || x.alibi_slopes) ? (mask != nullptr ? 2 : x.softcap > 0.f ? 3 : 4)
                    : (mask != nullptr || !(scale > 0.f)) ? 1 : 0;
-  // stage the mask through LDS when the workgroup's 32 rows share mask rows across its heads
-  p.mask_lds = mode == 1 && mask != nullptr && p.mask_vec && s.mask[1] == 0 && rows_pb == 32 &&
-               32 * s.mask[2] * 4 < INT32_MAX;
+  // stage the mask through LDS when the workgroup's rows share mask rows across its heads and
+  // their count is the one the kernel stages (64 for 8 waves, else 32)
+  const int64_t mask_rows = nw == 8 ? 64 : 32;
+  p.mask_lds = mode == 1 && mask != nullptr && p.mask_vec && s.mask[1] == 0 && rows_pb == mask_rows &&
+               mask_rows * s.mask[2] * 4 < INT32_MAX;
   KernelFn fn = bf16 ? (d == 64 ? pick_nw<true, 64>(nw, mode) : pick_nw<true, 128>(nw, mode))
                      : (d == 64 ? pick_nw<false, 64>(nw, mode) : pick_nw<false, 128>(nw, mode));
   // A plain fp32 call that one-wave workgroups already spread over the CUs is bound by each
