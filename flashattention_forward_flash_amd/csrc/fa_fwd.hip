@@ -415,7 +415,7 @@ struct Wave {
   float pw[BF16 ? 1 : 2][16];  // fp32 weights (fp32 path)
 
   __device__ __forceinline__ void init(const Params &p, int b, int head, int row0_wave, int lane_,
-                                       bool with_sink, int dpart_ = 0) {
+                                       bool with_sink, int dpart_ = 0, bool load_q = true) {
     lane = lane_;
     dpart = dpart_;
     half = lane >> 5;
@@ -445,7 +445,9 @@ struct Wave {
 
     const unsigned char *qrow = static_cast<const unsigned char *>(p.q) +
                                 ((int64_t)b * p.sq_b + (int64_t)head * p.sq_h + (p.q_start + row) * p.sq_t) * ES;
-    if constexpr (BF16) {
+    if (!load_q) {
+      // a wave that never computes scores
+    } else if constexpr (BF16) {
 #pragma unroll
       for (int ds = 0; ds < D / 16; ++ds) {
         u32x4 val = {0u, 0u, 0u, 0u};
@@ -559,6 +561,25 @@ struct Wave {
           for (int kb = 0; kb < 2; ++kb)
             dst[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[kb][e], qf[4 * c + e], dst[kb], 0, 0, 0);
       }
+    }
+  }
+
+  // fp32: S^T of key block kb alone, by the MFMA chain qk() runs for that block (same
+  // operands, same order, so the same bits).
+  // `hook(c)` runs before chunk c's MFMAs (the caller spreads its copies there).
+  template <typename Hook>
+  __device__ __forceinline__ void qk_block(const unsigned char *kl, int kb, f32x16 &dst, Hook &&hook) const {
+    static_assert(!BF16, "fp32 score waves");
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dst[r] = 0.f;
+    const int key = kb * 32 + lq;
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+      hook(c);
+      const int ch = (half * (D / 8) + c) ^ L::ksw(key);
+      const f32x4 a4 = *reinterpret_cast<const f32x4 *>(kl + key * (D * 4) + ch * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[e], qf[4 * c + e], dst, 0, 0, 0);
     }
   }
 
@@ -680,30 +701,30 @@ struct Wave {
 
   // fp32 kernels: the tile's weights exp2(x - shift) in base-2 units (the B operand of the PV
   // MFMAs) and this half's partial denominator.
-  __device__ __forceinline__ float expw(const Params &p, const f32x16 (&sc)[2], float shift) {
-    static_assert(!BF16, "bf16 kernels take softmax_pv");
-    float w[2][16];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if constexpr (MODE == 0)
-          w[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i], p.scale_log2, -shift));
-        else if constexpr (MODE == 1)
-          w[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i], kLog2e, -shift));
-        else
-          w[kb][i] = __builtin_amdgcn_exp2f(sc[kb][i] - shift);
-      }
+  __device__ __forceinline__ float expw_one(const Params &p, float x, float shift) const {
+    if constexpr (MODE == 0) return __builtin_amdgcn_exp2f(__builtin_fmaf(x, p.scale_log2, -shift));
+    else if constexpr (MODE == 1) return __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -shift));
+    else return __builtin_amdgcn_exp2f(x - shift);
+  }
+  // the partial denominator: the 32 weights summed as a fixed tree
+  __device__ __forceinline__ static float wsum(const float (&w)[2][16]) {
     float s8[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       s8[j] = (w[j >> 2][4 * (j & 3)] + w[j >> 2][4 * (j & 3) + 1]) +
               (w[j >> 2][4 * (j & 3) + 2] + w[j >> 2][4 * (j & 3) + 3]);
+    return ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+  }
+  __device__ __forceinline__ float expw(const Params &p, const f32x16 (&sc)[2], float shift) {
+    return expw(p, sc, shift, pw);
+  }
+  __device__ __forceinline__ float expw(const Params &p, const f32x16 (&sc)[2], float shift, float (&wout)[2][16]) {
+    static_assert(!BF16, "bf16 kernels take softmax_pv");
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) pw[kb][i] = w[kb][i];
-    return ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+      for (int i = 0; i < 16; ++i) wout[kb][i] = expw_one(p, sc[kb][i], shift);
+    return wsum(wout);
   }
 
   // The reference point m of the online softmax.  It moves only when the tile's row maximum
@@ -744,18 +765,28 @@ struct Wave {
   // and the weights are recomputed for the rows whose m moved.  Both ways give the same bits.
   // MODE 2-4 take the maximum first: under ALiBi the reference point of many rows moves at
   // every tile.
-  __device__ __forceinline__ float weights(const Params &p, const f32x16 (&sc)[2]) {
-    float lsum = 0.f;
-    if constexpr (MODE < 2) {
-      lsum = expw(p, sc, m_run == -INFINITY ? 0.f : m_run);
-      if (!__ballot(m_run == -INFINITY || !(lsum < kLazyW))) {
-        l_run = __builtin_fmaf(1.f, l_run, lsum);
-        return 1.f;
-      }
+  __device__ __forceinline__ float weights(const Params &p, const f32x16 (&sc)[2]) { return weights(p, sc, pw); }
+  __device__ __forceinline__ float weights(const Params &p, const f32x16 (&sc)[2], float (&wout)[2][16]) {
+    if constexpr (MODE < 2) return weights_rest(p, sc, expw(p, sc, m_run == -INFINITY ? 0.f : m_run, wout), wout);
+    float shift, alpha;
+    const float m_new = ref_point(p, sc, shift, alpha);
+    const float lsum = expw(p, sc, shift, wout);
+    l_run = __builtin_fmaf(alpha, l_run, lsum);
+    m_run = m_new;
+    return alpha;
+  }
+  // MODE 0 and 1: weights() once the weights against the current m (and their sum lsum) are
+  // in wout.
+  __device__ __forceinline__ float weights_rest(const Params &p, const f32x16 (&sc)[2], float lsum,
+                                                float (&wout)[2][16]) {
+    static_assert(MODE < 2, "lazy reference point");
+    if (!__ballot(m_run == -INFINITY || !(lsum < kLazyW))) {
+      l_run = __builtin_fmaf(1.f, l_run, lsum);
+      return 1.f;
     }
     float shift, alpha;
     const float m_new = ref_point(p, sc, shift, alpha);
-    if (MODE >= 2 || __ballot(m_new != m_run)) lsum = expw(p, sc, shift);
+    if (__ballot(m_new != m_run)) lsum = expw(p, sc, shift, wout);
     l_run = __builtin_fmaf(alpha, l_run, lsum);
     m_run = m_new;
     return alpha;
@@ -863,7 +894,8 @@ struct Wave {
 
   // fp32 kernels: O^T += V^T P^T with the tile's V in `vl`.  MFMA (kb, i) contracts 2 keys:
   // lane half h supplies key 32kb + 8(i/4) + 4h + i%4.
-  __device__ __forceinline__ void pv(const unsigned char *vl) {
+  __device__ __forceinline__ void pv(const unsigned char *vl) { pv(vl, pw); }
+  __device__ __forceinline__ void pv(const unsigned char *vl, const float (&win)[2][16]) {
     static_assert(!BF16, "bf16 kernels take softmax_pv");
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -875,9 +907,33 @@ struct Wave {
           const int d = (dpart * NOB + db) * 32 + lq;
           const int ch = (d >> 2) ^ L::vsw(key);
           const float a = *reinterpret_cast<const float *>(vl + key * (D * 4) + ch * 16 + (d & 3) * 4);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pw[kb][i], oacc[db], 0, 0, 0);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, win[kb][i], oacc[db], 0, 0, 0);
         }
       }
+  }
+  // fp32 MODE 0 and 1: PV of the previous tile (V in `vl`, its weights `win`) and the weights of
+  // the current tile's scores `sc` against the current m (the first step of weights(), into
+  // `wout`), in one stretch of code so that the vector work runs beside the MFMAs.  Returns the
+  // weights' partial sum, for weights_rest().
+  __device__ __forceinline__ float pv_expw(const Params &p, const unsigned char *vl, const float (&win)[2][16],
+                                           const f32x16 (&sc)[2], float (&wout)[2][16]) {
+    static_assert(!BF16 && MODE < 2, "fp32, lazy reference point");
+    const float shift = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+#pragma unroll
+        for (int db = 0; db < NOB; ++db) {
+          const int d = (dpart * NOB + db) * 32 + lq;
+          const int ch = (d >> 2) ^ L::vsw(key);
+          const float a = *reinterpret_cast<const float *>(vl + key * (D * 4) + ch * 16 + (d & 3) * 4);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, win[kb][i], oacc[db], 0, 0, 0);
+        }
+        wout[kb][i] = expw_one(p, sc[kb][i], shift);
+      }
+    return wsum(wout);
   }
   // transposing read of keys 16c + 8e + key_l (immediate offset), see softmax_pv()
   __device__ __forceinline__ static s16x4 read_v(uint32_t a, int c, int e) {
@@ -1208,6 +1264,167 @@ fa_fwd_kernel(Params p0) {
   if (MODE != 1 && cp.template src<true>(p, wk.t_end - 1).inside) run(std::integral_constant<bool, MODE != 1>{});
   else run(std::false_type{});
   wv.finish(p, wk.b, head, wk.split);
+}
+
+// ---------------------------------------------------------------------------------------
+// fp32, one 32-row block of one head per workgroup of 4 waves with split roles.  An fp32 tile
+// costs a wave 2 x (D / 2) MFMAs for the scores of its two 32-key blocks and 2 x D / 2 more for
+// the PV product, one chain after the other, which makes a lone block's serial chain long.
+// Here waves 0 and 1 compute the scores of key block 0 and 1 (Wave::qk_block: the chain of
+// Wave::qk for that block) one tile ahead and hand them over through LDS, while waves 2 and 3
+// keep the rows' online-softmax state and the output for their half of d (the arithmetic of
+// the d-part waves, DP = 2).  A softmax wave issues the PV MFMAs of tile u - 1 and then takes
+// the softmax step of tile u, whose vector work runs beside those MFMAs; the output sees the
+// same operations in the same order (rescale for u - 1, PV of u - 1, rescale for u, ...), so
+// every row gets the bits of the one-wave kernel.
+//
+// Step u (from t_begin - 1 to t_end; one barrier each): the score waves compute S(u + 1) from
+// K(u + 1) and, between the MFMAs of that chain, copy K(u + 2) and V(u); the softmax waves
+// issue PV(u - 1) from V(u - 1) and the weights of u - 1 together with tile u's weights against
+// the current m (Wave::pv_expw), then finish the softmax step of u.  Tile t lives in K, V, S
+// and weight buffers (t - t_begin) % 2, so a step writes only buffers that the step before it
+// was the last to read.
+// ---------------------------------------------------------------------------------------
+constexpr int kSBytes = 2 * 16 * 64 * 4;  // S^T of one tile: [key block][register / 4][lane][4] fp32
+
+template <int D>
+__global__ void __launch_bounds__(320) fa_fwd_so_kernel(Params p0) {
+  using L = Layout<false, D>;
+  using CP = Copier<false, D, 1>;  // wave 4 copies the tiles
+  __shared__ __attribute__((aligned(1024))) unsigned char k0[L::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char k1[L::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char v0[L::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char v1[L::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char s0[kSBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char s1[kSBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  Work wk(p0);
+  const Params p = seq_params(p0, wk.b);
+  wk.set_range(p);
+  if (wk.t_begin >= wk.t_end) {  // no key for these rows: zeros and -inf
+    if (wid == 2 || wid == 3) {
+      Wave<false, D, 0, 2> wv;
+      wv.init(p, wk.b, wk.head_base, wk.row0_blk, lane, true, wid - 2);
+      wv.finish(p, wk.b, wk.head_base, 0);
+    }
+    return;
+  }
+  const int head = wk.head_base;  // one head per workgroup
+
+  // The step schedule, one barrier per step, the same for every wave; each role runs it in a
+  // loop of its own, so that no role's registers stay live through another's work.
+  // body(u, kr, sw, sr, vr, wr, wn, kw, vw); j = u - t_begin + 1 even: tile u + 1 is in slot 0,
+  // tiles u and u - 1 in slots 1 and 0.
+  auto run = [&](auto &&body, float (&w0)[2][16], float (&w1)[2][16]) __attribute__((always_inline)) {
+    for (int u = wk.t_begin - 1; u <= wk.t_end; u += 2) {
+      body(u, k0, s0, s1, v0, w0, w1, k1, v1);
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's copies and LDS writes are done
+      __syncthreads();                // ... everyone's, and the buffers read in this step are free
+      if (u + 1 <= wk.t_end) {
+        body(u + 1, k1, s1, s0, v1, w1, w0, k0, v0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    }
+  };
+
+  if (wid == 4) {
+    // copy wave: K(t_begin) first, then K(u + 2) and V(u) in step u
+    CP cp;
+    cp.init(p, wk.b, wk.kvh, 0, lane);
+    {
+      const typename CP::Src ks = cp.template src<true>(p, wk.t_begin);
+      const uint32_t wo = cp.wave_off();
+#pragma unroll
+      for (int i = 0; i < CP::BPW; ++i) cp.template copy_k<false>(ks, i, k0, wo);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    float wd[2][16];
+    run([&](int u, const unsigned char *, unsigned char *, const unsigned char *, const unsigned char *,
+            float (&)[2][16], float (&)[2][16], unsigned char *kw, unsigned char *vw) __attribute__((always_inline)) {
+          // a tile wholly inside the keys by global loads (its base address in SGPRs, no vector
+          // work per copy), else through the buffer resource.  The lane offsets pass through
+          // empty asm statements, so that the compiler keeps them 32-bit (see fa_fwd_kernel).
+#pragma unroll
+          for (int i = 0; i < CP::BPW; ++i) {
+            asm("" : "+v"(cp.koff[i]));
+            asm("" : "+v"(cp.voff[i]));
+          }
+          const uint32_t wo = cp.wave_off();
+          if (u + 2 < wk.t_end) {
+            const typename CP::Src ks = cp.template src<true>(p, u + 2);
+            if (ks.inside) {
+#pragma unroll
+              for (int i = 0; i < CP::BPW; ++i) cp.template copy_k<true>(ks, i, kw, wo);
+            } else {
+#pragma unroll
+              for (int i = 0; i < CP::BPW; ++i) cp.template copy_k<false>(ks, i, kw, wo);
+            }
+          }
+          if (u >= wk.t_begin && u < wk.t_end) {
+            const typename CP::Src vs = cp.template src<false>(p, u);
+            if (vs.inside) {
+#pragma unroll
+              for (int i = 0; i < CP::BPW; ++i) cp.template copy_v<true>(vs, i, vw, wo);
+            } else {
+#pragma unroll
+              for (int i = 0; i < CP::BPW; ++i) cp.template copy_v<false>(vs, i, vw, wo);
+            }
+          }
+        }, wd, wd);
+    return;
+  }
+  if (wid < 2) {
+    // score waves: S(u + 1) in step u
+    Wave<false, D, 0, 2> wv;
+    wv.init(p, wk.b, head, wk.row0_blk, lane, false);
+    __syncthreads();  // K(t_begin) has landed
+    float wd[2][16];
+    run([&](int u, const unsigned char *kr, unsigned char *sw, const unsigned char *, const unsigned char *,
+            float (&)[2][16], float (&)[2][16], unsigned char *, unsigned char *) __attribute__((always_inline)) {
+          if (u + 1 < wk.t_end) {
+            f32x16 sc;
+            wv.qk_block(kr, wid, sc, [](int) {});
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 v4 = {sc[4 * g], sc[4 * g + 1], sc[4 * g + 2], sc[4 * g + 3]};
+              *reinterpret_cast<f32x4 *>(sw + ((wid * 4 + g) * 64 + lane) * 16) = v4;
+            }
+          }
+        }, wd, wd);
+    return;
+  }
+  // softmax waves: PV(u - 1) and the softmax step of u in step u
+  Wave<false, D, 0, 2> wv;
+  wv.init(p, wk.b, head, wk.row0_blk, lane, true, wid - 2, false);
+  __syncthreads();  // K(t_begin) has landed
+  float w0[2][16], w1[2][16];  // the weights of the tiles in slot 0 and 1
+  run([&](int u, const unsigned char *, unsigned char *, const unsigned char *sr, const unsigned char *vr,
+          float (&wr)[2][16], float (&wn)[2][16], unsigned char *, unsigned char *) __attribute__((always_inline)) {
+        const bool pv_due = u - 1 >= wk.t_begin, sm_due = u >= wk.t_begin && u < wk.t_end;
+        if (sm_due) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 v4 = *reinterpret_cast<const f32x4 *>(sr + ((kb * 4 + g) * 64 + lane) * 16);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) wv.sacc[kb][4 * g + e] = v4[e];
+            }
+          if (!wv.full(u)) wv.select(u, wv.sacc);
+        }
+        if (pv_due && sm_due) {
+          const float lsum = wv.pv_expw(p, vr, wr, wv.sacc, wn);  // PV(u - 1) beside tile u's weights
+          wv.rescale(wv.weights_rest(p, wv.sacc, lsum, wn));
+        } else if (pv_due) {
+          wv.pv(vr, wr);
+        } else if (sm_due) {
+          wv.rescale(wv.weights(p, wv.sacc, wn));
+        }
+      }, w0, w1);
+  wv.finish(p, wk.b, head, 0);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1598,13 +1815,13 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   KernelFn fn = bf16 ? (d == 64 ? pick_nw<true, 64>(nw, mode) : pick_nw<true, 128>(nw, mode))
                      : (d == 64 ? pick_nw<false, 64>(nw, mode) : pick_nw<false, 128>(nw, mode));
   // A plain fp32 call that one-wave workgroups already spread over the CUs is bound by each
-  // wave's chain of fp32 MFMAs: there d / 32 waves share each 32-row block, every one computing
-  // the scores and weights and its own 32 columns of the output (the same bits, a chain
-  // shorter by 3/8 at d = 128: the 511-token, 16-head prefill takes ≈ 27 % less time).
+  // block's serial chain of fp32 MFMAs: there the split-role kernel runs each 32-row block on
+  // 4 waves (two computing scores a tile ahead, two the softmax and PV for half of d each; the
+  // same bits).
   int waves = nw;
   if (auto_geom && !bf16 && mode == 0 && nw == 1) {
-    waves = (int)(d / 32);
-    fn = d == 64 ? fa_fwd_kernel<false, 64, 2, 0, 2> : fa_fwd_kernel<false, 128, 4, 0, 4>;
+    waves = 5;
+    fn = d == 64 ? fa_fwd_so_kernel<64> : fa_fwd_so_kernel<128>;
   }
   if (!launch) return FA_OK;
   (void)hipGetLastError();  // clear a stale error so the check below reports this launch

@@ -97,15 +97,18 @@ def test_layout_invariant(dtype):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_output_d_parts_equal_one_wave(d):
-    """Small fp32 calls whose automatic geometry is one-wave workgroups run with d / 32 waves per
-    32-row block, each computing the scores and weights and its own 32 output columns: the same
-    bits as the one-wave tiling, and the oracle's values."""
+    """Small fp32 calls whose automatic geometry is one-wave workgroups run on the split-role
+    kernel (two waves computing the scores of the two 32-key blocks a tile ahead, two taking the
+    softmax step and the PV product for half of d each, one copying the tiles): the same bits as
+    the one-wave tiling, and the oracle's values.  Cases: causal, offset rows, decode-like,
+    non-causal ragged, window with sinks, a call whose rows see no key, a single partial tile."""
     import oracle
     from gpu_common import compare, host, scale_for
     B, Hq, Hkv = 1, 4, 2
     for Tq, Tk, flags in ((100, 100, dict(causal=True)), (65, 300, dict(causal=True, q_offset=235)),
                           (1, 1000, dict(causal=True, q_offset=999)), (70, 129, dict(causal=False)),
-                          (50, 500, dict(causal=True, window=64, q_offset=400, sinks=True))):
+                          (50, 500, dict(causal=True, window=64, q_offset=400, sinks=True)),
+                          (40, 64, dict(causal=True, window=50, q_offset=200)), (33, 7, dict(causal=False))):
         q, k, v, z = make_inputs(f"inv-dparts/{d}/{Tq}/{Tk}", B, Hq, Hkv, Tq, Tk, d, "f32", sinks=True)
         tq, tk, tv = dev(q), dev(k), dev(v)
         kw = dict(flags)
