@@ -565,9 +565,24 @@ def _leg_decode(B, Hq, Hkv, Tk, d, dtype):
                                        causal=True, out=out, lse=lse)), nbytes, 4.0 * d * B * Hq * Tk
 
 
+def _leg_noncausal():
+    """The mask run's inputs without the mask (non-causal): the HBM bytes the mask adds are the
+    difference between the two legs' counters."""
+    import torch
+    import flashattention_forward_flash_amd as fa
+    B, Hq, Hkv, T, d = 8, 32, 8, 8192, 128
+    q, k, v = _inputs("c5", B, Hq, Hkv, T, T, d, "bf16")
+    out = torch.empty_like(q)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    nbytes = 2 * (q.numel() + k.numel() + v.numel() + out.numel())
+    return (lambda: fa.forward(q, k, v, scale=scale, causal=False, out=out, return_lse=False)), \
+        nbytes, 4.0 * d * B * Hq * T * T
+
+
 LEGS = {
     "headline": _leg_headline,
     "mask": _leg_mask,
+    "noncausal": _leg_noncausal,
     "prefill511_f32": lambda: _leg_prefill(511, "f32"),
     "prefill2044_f32": lambda: _leg_prefill(2044, "f32"),
     "prefill2044_bf16": lambda: _leg_prefill(2044, "bf16"),
@@ -615,6 +630,11 @@ def _csv_rows(path):
         return list(csv.DictReader(f))
 
 
+def _ours(name):
+    """A kernel of the library (the forward kernels and the split-KV merge)."""
+    return any(k in name for k in ("fa_fwd_kernel", "fa_fwd_so_kernel", "fa_merge_kernel"))
+
+
 def _short(name):
     name = name.replace("(anonymous namespace)::", "").replace("void ", "")
     return name.split("(")[0]
@@ -625,11 +645,11 @@ def _write_trace_summary(d, leg, src):
     (what bench.py's per-launch timing compares to) and rocprofv3's own --stats line."""
     meta = json.loads(open(os.path.join(d, f"{leg}_trace", "leg.json")).read().strip().splitlines()[-1])
     trace = sorted((r for r in _csv_rows(os.path.join(d, f"{leg}_trace", "run_kernel_trace.csv"))
-                    if "fa_fwd_kernel" in r["Kernel_Name"]), key=lambda r: int(r["Start_Timestamp"]))
+                    if _ours(r["Kernel_Name"])), key=lambda r: int(r["Start_Timestamp"]))
     us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace]
     timed = us[meta["warmup"]:]
     stats = [r for r in _csv_rows(os.path.join(d, f"{leg}_trace", "run_kernel_stats.csv"))
-             if "fa_fwd_kernel" in r["Name"]]
+             if _ours(r["Name"])]
     flops = meta["flops"]
     lines = ["# fa_fwd kernel, bf16, d = 128, causal, B = 8, Hq = 32, Hkv = 8, Tq = Tk = 8192", "",
              "Kernel trace of the headline workload (one call = one step of `bench.py`).", "",
@@ -704,7 +724,7 @@ def write_profile_summaries(d):
         steps, warmup = meta["steps"], meta["warmup"]
         # the library's kernels only (torch's setup copies of the inputs are not part of a step)
         trace = [r for r in _csv_rows(os.path.join(d, f"{leg}_trace", "run_kernel_trace.csv"))
-                 if "fa_fwd_kernel" in r["Kernel_Name"] or "fa_merge_kernel" in r["Kernel_Name"]]
+                 if _ours(r["Kernel_Name"])]
         trace.sort(key=lambda r: int(r["Start_Timestamp"]))
         per_step = len(trace) // (steps + warmup)
         timed = trace[warmup * per_step:]
@@ -713,7 +733,7 @@ def write_profile_summaries(d):
         byts = {}
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             per = {key: v for key, v in counter_kib(f"{leg}_{c}").items()
-                   if "fa_fwd_kernel" in key[1] or "fa_merge_kernel" in key[1]}
+                   if _ours(key[1])}
             ids = sorted(per)[warmup * per_step:]
             byts[c] = sum(per[i][c] for i in ids) * 1024 * scale[c] / steps
         total = byts["FETCH_SIZE"] + byts["WRITE_SIZE"]
