@@ -23,6 +23,8 @@
 //    lane-local.  For bf16, V stays row-major in LDS and each lane gathers its V^T operand
 //    with transposing LDS reads (ds_read_b64_tr_b16).
 //  * Online softmax in base 2: x = s * scale * log2(e); p = exp2(x - m) on the hardware exp2.
+//    With an additive mask (MODE 1) s is q.k + fl(mask * fl(1 / scale)), the mask term being
+//    the accumulators' starting value, so x = scale (q.k + mask / scale) log2(e).
 //    The reference point m moves only when a tile's maximum exceeds it by more than kLazy;
 //    alpha = exp2(m_old - m_new) is then exactly 1 when m does not move and 0 when m_old =
 //    -inf (the guards of "Fused attention and softmax", exact definition steps 2 and 5);
@@ -37,11 +39,12 @@
 //    states merged by fa_merge_kernel), paged K/V (each tile's rows found through a block
 //    table), packed sequences and per-sequence lengths (seq_params): they change which tiles
 //    a work item visits and where a tile is read from, never the arithmetic of a row.
-//  * Kernels: MODE 0 (no mask, scale > 0: raw-maximum shortcut), MODE 1 (additive mask or
-//    scale <= 0: explicit scores), MODE 2 (softcap / ALiBi score variants, any mask), and for
-//    bf16 4- and 8-wave workgroups MODE 3 (softcap, with or without ALiBi) and MODE 4 (ALiBi
-//    alone) without a mask: the same arithmetic as MODE 2 with less code, which lets the
-//    4-wave kernels run two waves per SIMD.
+//  * Kernels: MODE 0 (no mask, scale > 0: raw-maximum shortcut), MODE 1 (additive mask,
+//    scale > 0: the score accumulators start at mask / scale, then as MODE 0), MODE 2 (softcap
+//    / ALiBi score variants, any mask, and any scale <= 0: explicit scores), and for bf16 4-
+//    and 8-wave workgroups MODE 3 (softcap, with or without ALiBi) and MODE 4 (ALiBi alone)
+//    without a mask: the same arithmetic as MODE 2 with less code, which lets the 4-wave
+//    kernels run two waves per SIMD.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -95,9 +98,9 @@ struct Params {
   int32_t causal;
   int32_t mask_vec;        // mask rows contiguous and 16-byte aligned: read 4 entries at a time
   int32_t tile_major;      // > 0: blocked order for a mask shared by every (b, h), this many slices per block
-  int32_t mask_lds;        // MODE 1: each tile's 32 x 64 mask block is staged in LDS (MaskCopier)
+  int32_t mask_lds;        // MODE 1: each tile's mask block is staged in LDS (MaskStager)
   float scale_log2;        // scale * log2(e)
-  float scale;             // scale (MODE 1 scores are scale q.k + mask, in natural units)
+  float inv_scale;         // 1 / scale (MODE 1: the mask enters the score accumulators as mask / scale)
   // Split-KV ("FlashAttention forward in C", "Going further": split-KV / Flash-Decoding).
   // n_splits = 0: no split, rows end in o and lse.  Otherwise key split s is the absolute key
   // range [64 s split_tiles, 64 (s + 1) split_tiles); a work item covers one split and writes
@@ -257,11 +260,16 @@ __device__ __forceinline__ void glb_load_lds16(const unsigned char *base, unsign
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(base + off),
                                    (__attribute__((address_space(3))) void *)lds_block, 16, 0, 0);
 }
+// 16 bytes per lane into registers through a resource (bytes past its range read as zeros)
+__device__ __forceinline__ u32x4 buf_load16(BufRsrc rs, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+}
 #else
 typedef int BufRsrc;
 __device__ inline BufRsrc make_rsrc(const unsigned char *, int64_t) { return 0; }
 __device__ inline void buf_load_lds16(BufRsrc, unsigned char *, uint32_t) {}
 __device__ inline void glb_load_lds16(const unsigned char *, unsigned char *, uint32_t) {}
+__device__ inline u32x4 buf_load16(BufRsrc, uint32_t) { return u32x4{0u, 0u, 0u, 0u}; }
 #endif
 
 
@@ -491,10 +499,12 @@ struct Wave {
   // steps, so that the wave never stalls on a full memory-issue queue.
   template <bool PIPE, typename Hook>
   __device__ __forceinline__ void qk(const unsigned char *kl, f32x16 (&dst)[2], Hook &&hook) const {
+    if constexpr (MODE != 1) {  // MODE 1: mask_acc() filled them
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dst[kb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) dst[kb][r] = 0.f;
+    }
     if constexpr (BF16 && PIPE) {
       // K operand of step ds for both key blocks: row kb * 32 + lq, chunk (2 ds + half) swizzled
       // by the row (key % chunks-per-row is lq % chunks-per-row for both blocks).
@@ -591,32 +601,16 @@ struct Wave {
   // MODE 0 (no mask, scale > 0): the scores stay raw dot products; the row maximum is taken on
   //   them (scaling by a positive constant commutes with max and with fp32 rounding) and each
   //   weight is exp2(fma(s, scale log2 e, -m)).
-  // MODE 1 (additive mask, or scale <= 0): y = fma(s, scale, mask) in natural units; the
-  //   row maximum is taken on y and each weight is exp2(fma(y, log2 e, -m)).
-  // MODE 2-4 (softcap or ALiBi): x = [c log2 e tanh(s scale / c) | s scale log2 e]
+  // MODE 1 (additive mask, scale > 0): the score accumulators start at mask / scale (mask_acc)
+  //   and the MFMAs add q.k to them, so y = scale (q.k + mask / scale); from there on, MODE 0.
+  // MODE 2-4 (softcap or ALiBi, or scale <= 0): x = [c log2 e tanh(s scale / c) | s scale log2 e]
   //   + dist (-slope log2 e) + mask log2 e (MODE 2 only: 3 and 4 have no mask).
-  __device__ __forceinline__ void scores(const Params &p, int t, f32x16 (&sc)[2],
-                                        const unsigned char *ml) const {
+  __device__ __forceinline__ void scores(const Params &p, int t, f32x16 (&sc)[2]) const {
     if constexpr (MODE >= 2) {
       variants(p, t, sc);
       if (MODE != 2 || !p.mask) return;
-    }
-    if constexpr (MODE == 1 || MODE == 2) {
       float mv[2][16];
-      if (MODE == 1 && p.mask_lds) {
-        // the row's 64 entries of the staged block: logical 16-byte chunk c of LDS row r sits at
-        // chunk c ^ (r % 16); registers 4g..4g+3 of key block kb are chunk 8 kb + 2 g + half
-        const uint32_t r = mask_lds_row;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const uint32_t c = (uint32_t)(kb * 8 + 2 * g + half) ^ (r & 15u);
-            const f32x4 m4 = *reinterpret_cast<const f32x4 *>(ml + r * 256u + c * 16u);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) mv[kb][4 * g + e] = m4[e];
-          }
-      } else if (mrow && p.mask_vec && t * kBc + kBc <= p.Tk) {
+      if (mrow && p.mask_vec && t * kBc + kBc <= p.Tk) {
         // registers 4g..4g+3 of a block hold 4 consecutive keys: one 16-byte read
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -636,17 +630,52 @@ struct Wave {
             mv[kb][i] = (mrow && row_ok && key < p.Tk) ? mrow[(int64_t)key * p.sm_j] : 0.f;
           }
       }
-      if constexpr (MODE == 1) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sc[kb][i] = __builtin_fmaf(sc[kb][i], p.scale, mv[kb][i]);
-      } else {
+        for (int i = 0; i < 16; ++i) sc[kb][i] = sc[kb][i] + mv[kb][i] * kLog2e;
+    }
+  }
+  // MODE 1: the score accumulators of tile t before its QK MFMAs, mask / scale per entry
+  // (entries past the mask's end and rows past Tq: 0).  From the staged LDS block, whose
+  // entries the stager already divided (the same product, fl(mask * fl(1 / scale))), or from
+  // the mask rows in global memory.
+  __device__ __forceinline__ void mask_acc(const Params &p, int t, const unsigned char *ml,
+                                           f32x16 (&sc)[2]) const {
+    static_assert(MODE == 1, "additive mask in the accumulators");
+    if (p.mask_lds) {
+      // the row's 64 entries of the staged block: logical 16-byte chunk c of LDS row r sits at
+      // chunk c ^ (r % 16); registers 4g..4g+3 of key block kb are chunk 8 kb + 2 g + half
+      const uint32_t r = mask_lds_row;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sc[kb][i] = sc[kb][i] + mv[kb][i] * kLog2e;
-      }
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t c = (uint32_t)(kb * 8 + 2 * g + half) ^ (r & 15u);
+          const f32x4 m4 = *reinterpret_cast<const f32x4 *>(ml + r * 256u + c * 16u);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[kb][4 * g + e] = m4[e];
+        }
+      return;
+    }
+    if (mrow && p.mask_vec && t * kBc + kBc <= p.Tk) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 m4 = {0.f, 0.f, 0.f, 0.f};
+          if (row_ok) m4 = *reinterpret_cast<const f32x4 *>(mrow + t * kBc + kb * 32 + 8 * g + 4 * half);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[kb][4 * g + e] = m4[e] * p.inv_scale;
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = t * kBc + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+          sc[kb][i] = ((mrow && row_ok && key < p.Tk) ? mrow[(int64_t)key * p.sm_j] : 0.f) * p.inv_scale;
+        }
     }
   }
   // MODE 2-4 before any mask: the capped logit and the ALiBi bias.  The distance |p - key| is
@@ -702,8 +731,7 @@ struct Wave {
   // fp32 kernels: the tile's weights exp2(x - shift) in base-2 units (the B operand of the PV
   // MFMAs) and this half's partial denominator.
   __device__ __forceinline__ float expw_one(const Params &p, float x, float shift) const {
-    if constexpr (MODE == 0) return __builtin_amdgcn_exp2f(__builtin_fmaf(x, p.scale_log2, -shift));
-    else if constexpr (MODE == 1) return __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -shift));
+    if constexpr (MODE <= 1) return __builtin_amdgcn_exp2f(__builtin_fmaf(x, p.scale_log2, -shift));
     else return __builtin_amdgcn_exp2f(x - shift);
   }
   // the partial denominator: the 32 weights summed as a fixed tree
@@ -741,8 +769,7 @@ struct Wave {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
     // to base-2 units (a positive factor commutes with max and with fp32 rounding; -inf stays)
-    if constexpr (MODE == 0) mx = mx * p.scale_log2;
-    if constexpr (MODE == 1) mx = mx * kLog2e;
+    if constexpr (MODE <= 1) mx = mx * p.scale_log2;
     // The row maximum exceeds m + kLazy exactly when one lane half's maximum does, so the
     // exchange between the halves is only needed when some lane's does.
     float m_new = m_run;
@@ -803,8 +830,8 @@ struct Wave {
   }
 
   // fp32 kernels: the whole online-softmax step of tile t on `sacc`, then pv().
-  __device__ __forceinline__ void softmax(const Params &p, int t, const unsigned char *ml = nullptr) {
-    scores(p, t, sacc, ml);
+  __device__ __forceinline__ void softmax(const Params &p, int t) {
+    scores(p, t, sacc);
     if (!full(t)) select(t, sacc);
     rescale(weights(p, sacc));
   }
@@ -815,10 +842,9 @@ struct Wave {
   // chunk c's PV MFMAs, whose execution overlaps the vector work of chunk c + 1.  The MFMAs are
   // ordered key chunk outer, d block inner, so that consecutive MFMAs accumulate into different
   // registers.
-  __device__ __forceinline__ void softmax_pv(const Params &p, int t, const unsigned char *ml,
-                                             const unsigned char *vl) {
+  __device__ __forceinline__ void softmax_pv(const Params &p, int t, const unsigned char *vl) {
     static_assert(DP == 1, "bf16 kernels own the whole d range");
-    scores(p, t, sacc, ml);
+    scores(p, t, sacc);
     if (!full(t)) select(t, sacc);
     float shift, alpha;
     const float m_new = ref_point(p, sacc, shift, alpha);
@@ -860,8 +886,7 @@ struct Wave {
         for (int j = 0; j < 8; ++j) {
           const float x = sacc[c >> 1][8 * (c & 1) + j];
           float w;
-          if constexpr (MODE == 0) w = __builtin_amdgcn_exp2f(__builtin_fmaf(x, p.scale_log2, -shift));
-          else if constexpr (MODE == 1) w = __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -shift));
+          if constexpr (MODE <= 1) w = __builtin_amdgcn_exp2f(__builtin_fmaf(x, p.scale_log2, -shift));
           else w = __builtin_amdgcn_exp2f(x - shift);
           pb[c][j] = (__bf16)w;
         }
@@ -1105,38 +1130,52 @@ struct Copier {
 
 // ---------------------------------------------------------------------------------------
 // Mask tiles through LDS (MODE 1 when the workgroup's MR rows share their mask rows across its
-// heads, mask rows contiguous and 16-byte aligned): the MR x 64 fp32 block of tile t, row-major
-// 256 bytes per row with the 16-byte chunks of row r stored at chunk ^ (r % 16), is copied
-// like K and V (MR / 4 blocks of 4 rows, split over the waves).  MR is 64 for 8-wave
-// workgroups (two 32-row halves of 4 heads each), else 32.  Rows past Tq and entries past the
-// mask's last valid entry read as zeros; other entries past Tk belong to keys that the select
-// removes.
+// heads, mask rows contiguous and 16-byte aligned): the MR x 64 fp32 block of tile t, each
+// entry divided by the scale (fl(mask * fl(1 / scale)), the value mask_acc() starts the score
+// accumulators at), row-major 256 bytes per row with the 16-byte chunks of row r stored at
+// chunk ^ (r % 16).  The waves load the next tile's block into registers one tile ahead (MR / 4
+// blocks of 4 rows, split over the waves), divide it and write it to LDS at the end of the
+// step, so the division is done once per workgroup rather than once per head.  MR is 64 for
+// 8-wave workgroups (two 32-row halves of 4 heads each), else 32.  Rows past Tq and entries
+// past the mask's last valid entry read as zeros; other entries past Tk belong to keys that
+// the select removes.
 // ---------------------------------------------------------------------------------------
 template <int NW>
-struct MaskCopier {
+struct MaskStager {
   static constexpr int MR = NW == 8 ? 64 : 32;  // staged rows
-  static constexpr int MPW = MR / 4 / NW;       // 1 KiB blocks each wave copies per tile
+  static constexpr int MPW = MR / 4 / NW;       // 1 KiB blocks each wave stages per tile
   const unsigned char *base;          // mask row row0 of the workgroup, key 0
   int64_t bytes_to_end;               // from base to the end of entry (Tq - 1, Tk - 1)
-  int wid;
-  uint32_t off[MPW];
-  __device__ __forceinline__ void init(const Params &p, int b, int row0, int wid_, int lane) {
-    wid = wid_;
+  uint32_t off[MPW], lds_off[MPW];
+  __device__ __forceinline__ void init(const Params &p, int b, int row0, int wid, int lane) {
     base = reinterpret_cast<const unsigned char *>(p.mask + (int64_t)b * p.sm_b + (int64_t)row0 * p.sm_i);
     bytes_to_end = ((int64_t)(p.Tq - 1 - row0) * p.sm_i + p.Tk) * 4;
 #pragma unroll
     for (int i = 0; i < MPW; ++i) {
+      // lane l of block k holds stored chunk l % 16 of row 4 k + l / 16, i.e. logical chunk
+      // (l % 16) ^ (row % 16)
       const int r = (wid * MPW + i) * 4 + lane / 16;
       const uint32_t c = (uint32_t)(lane % 16) ^ (uint32_t)(r & 15);
       off[i] = (uint32_t)(r * p.sm_i * 4) + c * 16u;
+      lds_off[i] = (uint32_t)((wid * MPW + i) * 1024 + lane * 16);
     }
   }
   __device__ __forceinline__ BufRsrc rsrc(int t) const {
     const int64_t skip = (int64_t)t * kBc * 4;
     return make_rsrc(base + skip, bytes_to_end - skip);
   }
-  __device__ __forceinline__ void copy(BufRsrc rs, int i, unsigned char *dst) const {
-    buf_load_lds16(rs, dst + (wid * MPW + i) * 1024, off[i]);
+  __device__ __forceinline__ void load(BufRsrc rs, u32x4 (&v)[MPW]) const {
+#pragma unroll
+    for (int i = 0; i < MPW; ++i) v[i] = buf_load16(rs, off[i]);
+  }
+  __device__ __forceinline__ void store(const Params &p, const u32x4 (&v)[MPW], unsigned char *dst) const {
+#pragma unroll
+    for (int i = 0; i < MPW; ++i) {
+      f32x4 m4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m4[e] = __uint_as_float(v[i][e]) * p.inv_scale;
+      *reinterpret_cast<f32x4 *>(dst + lds_off[i]) = m4;
+    }
   }
 };
 
@@ -1164,7 +1203,7 @@ fa_fwd_kernel(Params p0) {
   __shared__ __attribute__((aligned(1024))) unsigned char k1[L::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char v0[L::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char v1[L::TILE_BYTES];
-  constexpr int MBYTES = MODE == 1 ? MaskCopier<NW>::MR * 256 : 16;  // staged mask blocks (MODE 1)
+  constexpr int MBYTES = MODE == 1 ? MaskStager<NW>::MR * 256 : 16;  // staged mask blocks (MODE 1)
   __shared__ __attribute__((aligned(1024))) unsigned char m0[MBYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char m1[MBYTES];
 
@@ -1184,12 +1223,11 @@ fa_fwd_kernel(Params p0) {
   wv.init(p, wk.b, head, wk.row0_blk + (wq / G) * kRowsWave, lane, wk.split == 0, wid % DP);
   CP cp;
   cp.init(p, wk.b, wk.kvh, wid, lane);
-  using MC = MaskCopier<NW>;
-  constexpr int NMC = MODE == 1 ? MC::MPW : 0;  // mask copies of a tile per wave
-  MC mc;
+  using MS = MaskStager<NW>;
+  MS ms;
   const bool mlds = MODE == 1 && p.mask_lds;
   if (mlds) {
-    mc.init(p, wk.b, wk.row0_blk, wid, lane);
+    ms.init(p, wk.b, wk.row0_blk, wid, lane);
     wv.mask_lds_row = (uint32_t)((wq / G) * kRowsWave + (lane & 31));
   }
 
@@ -1211,8 +1249,10 @@ fa_fwd_kernel(Params p0) {
       }
     }
     const typename CP::Src ks = cp.template src<true>(p, t + 1), vs = cp.template src<false>(p, t + 1);
-    BufRsrc mrs;
-    if (mlds) mrs = mc.rsrc(t + 1);
+    // MODE 1 with a staged mask: this wave's share of the next tile's block, loaded now and
+    // written to LDS (divided by the scale) at the end of the step
+    u32x4 mnv[MS::MPW];
+    if (mlds && has_next) ms.load(ms.rsrc(t + 1), mnv);
     auto copies = [&](int ds) {  // copy i goes with QK step i * NDS / NCP
       if (has_next) {
         const uint32_t wo = cp.wave_off();
@@ -1222,34 +1262,31 @@ fa_fwd_kernel(Params p0) {
             if (i < CP::BPW) cp.template copy_k<GLB>(ks, i, kn, wo);
             else cp.template copy_v<GLB>(vs, i - CP::BPW, vn, wo);
           }
-        if (mlds) {
-#pragma unroll
-          for (int i = 0; i < NMC; ++i)
-            if (i * NDS / NMC == ds) mc.copy(mrs, i, mnext);
-        }
       }
     };
     if (wv.active(t)) {
+      if constexpr (MODE == 1) wv.mask_acc(p, t, mcur, wv.sacc);
       wv.template qk<true>(kc, wv.sacc, copies);
       if constexpr (BF16) {
-        wv.softmax_pv(p, t, mcur, vc);
+        wv.softmax_pv(p, t, vc);
       } else {
-        wv.softmax(p, t, mcur);
+        wv.softmax(p, t);
         wv.pv(vc);
       }
     } else {
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) copies(ds);
     }
+    if (mlds && has_next) ms.store(p, mnv, mnext);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile t + 1 have landed
     __syncthreads();                // ... everyone's have, and buffers kc, vc are free again
   };
   if (wk.t_begin < wk.t_end) {
     cp.tiles(p, wk.t_begin, k0, v0);
     if (mlds) {
-      const BufRsrc mrs = mc.rsrc(wk.t_begin);
-#pragma unroll
-      for (int i = 0; i < NMC; ++i) mc.copy(mrs, i, m0);
+      u32x4 mv[MS::MPW];
+      ms.load(ms.rsrc(wk.t_begin), mv);
+      ms.store(p, mv, m0);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -1769,7 +1806,7 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   p.n_blocks = (int32_t)n_blocks;
   p.causal = causal ? 1 : 0;
   p.scale_log2 = scale * kLog2e;
-  p.scale = scale;
+  p.inv_scale = 1.f / scale;
   p.mask_vec = mask != nullptr && s.mask[3] == 1 && aligned(mask, 16) && s.mask[0] % 4 == 0 &&
                s.mask[1] % 4 == 0 && s.mask[2] % 4 == 0;
   p.tile_major = 0;
@@ -1801,12 +1838,11 @@ fa_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
   p.k_start = 0;
 
   const bool bf16 = dtype == FA_BF16;
-  // MODE 1 when scores need the explicit form: an additive mask, or a scale that is not
-  // positive (the raw-maximum shortcut needs scale > 0).
   // MODE 2-4 for the score variants: 2 with a mask, else 3 (softcap, with or without ALiBi) or
-  // 4 (ALiBi alone).
+  // 4 (ALiBi alone).  MODE 2 also serves a scale that is not positive (the raw-maximum form
+  // of MODE 0 and 1 needs scale > 0).  MODE 1 for an additive mask, MODE 0 without.
   const int mode = (x.softcap > 0.f || x.alibi_slopes) ? (mask != nullptr ? 2 : x.softcap > 0.f ? 3 : 4)
-                   : (mask != nullptr || !(scale > 0.f)) ? 1 : 0;
+                   : !(scale > 0.f) ? 2 : mask != nullptr ? 1 : 0;
   // stage the mask through LDS when the workgroup's rows share mask rows across its heads and
   // their count is the one the kernel stages (64 for 8 waves, else 32)
   const int64_t mask_rows = nw == 8 ? 64 : 32;

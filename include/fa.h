@@ -13,7 +13,12 @@
  *
  * where head h reads KV head floor(h / (Hq / Hkv)) (grouped-query attention) and the
  * e^{z_h} sink term is present only when `sinks` is given.  A mask entry of -inf removes
- * the key.  A row with no visible key and no sink gets o = 0 and lse = -inf.
+ * the key.  A row with no visible key and no sink gets o = 0 and lse = -inf.  With a mask and
+ * scale > 0 the score is formed as scale * (q_i . k_j + mask / scale), the mask term being
+ * the starting value of the dot product's accumulator: the same value up to fp32 rounding,
+ * except that a finite entry above FLT_MAX * scale overflows to +inf there (as a +inf entry,
+ * it makes its row NaN).
+
  *
  * It is computed one absolute key tile [64t, 64t + 64) at a time with the online softmax
  * of "FlashAttention forward in C" section 2.2 (and "IV.5: Flash attention", "Softmax
