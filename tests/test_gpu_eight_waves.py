@@ -115,3 +115,39 @@ def test_one_visible_key_returns_its_value(tiling):
         lo = np.minimum(vf[:, h // group, 0], vf[:, h // group, 1])
         hi = np.maximum(vf[:, h // group, 0], vf[:, h // group, 1])
         assert np.all(o1[:, h] >= lo) and np.all(o1[:, h] <= hi), f"head {h}"
+
+
+# persistent launches: the 8-wave bf16 d 128 kernel with at least two work items per CU walks
+# them in one workgroup per CU; (name, B, Hq, Hkv, Tq, Tk, q_offset, causal, window, sinks)
+PERSISTENT = [
+    ("causal_ragged_rows", 2, 32, 8, 2047, 2048, 1, True, 0, True),
+    ("window_offset", 4, 16, 4, 2000, 2560, 560, True, 200, False),
+    ("noncausal", 1, 32, 8, 4096, 1024, 0, False, 0, True),
+]
+
+
+@pytest.mark.parametrize("case", PERSISTENT, ids=[c[0] for c in PERSISTENT])
+def test_persistent_launch_equals_one_item_per_workgroup(case):
+    """Work-item counts of at least 512 (two rounds on 256 CUs) take the persistent launch of the
+    8-wave kernel: each row's bits equal the 4-wave kernel's (one workgroup per item), and a
+    sample of rows matches the oracle."""
+    name, B, Hq, Hkv, Tq, Tk, qo, causal, window, with_sinks = case
+    d = 128
+    assert B * Hkv * ((Tq + 63) // 64) >= 512 and Tk % 64 == 0
+    q, k, v, z = make_inputs(f"persistent/{name}", B, Hq, Hkv, Tq, Tk, d, "bf16", sinks=with_sinks)
+    tq, tk, tv, tz = dev(q), dev(k), dev(v), dev(z)
+    kw = dict(scale=scale_for(d), q_offset=qo, causal=causal, window=window, sinks=tz if with_sinks else None)
+    say("persistent", name)
+    o8, l8 = fa.forward(tq, tk, tv, **kw)  # automatic geometry: 8 waves, persistent
+    o4, l4 = fa.forward(tq, tk, tv, tiling=(32, 4), **kw)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o8), bits(o4)), "O differs from the one-item-per-workgroup launch"
+    assert np.array_equal(bits(l8), bits(l4)), "LSE differs from the one-item-per-workgroup launch"
+    rng = np.random.default_rng(11)
+    rows = np.stack([rng.integers(0, B, 64), rng.integers(0, Hq, 64), rng.integers(0, Tq, 64)], axis=1)
+    rows[:3] = [[0, 0, 0], [B - 1, Hq - 1, Tq - 1], [B - 1, 0, Tq // 2]]
+    o_ref, l_ref = oracle.attention(q, k, v, scale=kw["scale"], q_offset=qo, causal=causal, window=window,
+                                    sinks=z if with_sinks else None, rows=rows)
+    og, lg = host(o8), host(l8)
+    compare(og[rows[:, 0], rows[:, 1], rows[:, 2]], lg[rows[:, 0], rows[:, 1], rows[:, 2]], o_ref, l_ref, "bf16",
+            f"persistent {name}")
