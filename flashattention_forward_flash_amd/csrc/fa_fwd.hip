@@ -984,6 +984,40 @@ struct Wave {
     }
   }
 
+  // bf16, d 128, no split: finish()'s values, stored through this wave's 8 KiB of LDS at `epi`
+  // so that each global store writes four whole rows (16 bytes per lane) instead of 8 bytes per
+  // lane across 32 rows.  Row r's 16-byte chunk c sits at r * 256 + (c ^ (r % 16)) * 16 there.
+  __device__ __forceinline__ void finish_lds(const Params &p, int b, int head, int row0_wave, unsigned char *epi) {
+    static_assert(BF16 && D == 128 && DP == 1, "bf16 rows of 256 bytes");
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float r4[4];
+        // (+ 0 as in finish())
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r4[e] = oacc[db][4 * g + e] * inv + 0.f;
+        const u32x2 pk = {pack_bf16x2(r4[0], r4[1]), pack_bf16x2(r4[2], r4[3])};
+        // registers 4g..4g+3 hold d 32 db + 8 g + 4 half ..: bytes 8 half.. of chunk 4 db + g
+        const int c = 4 * db + g;
+        *reinterpret_cast<u32x2 *>(epi + lq * 256 + ((c ^ (lq & 15)) * 16) + 8 * half) = pk;
+      }
+    const unsigned char *obase = static_cast<unsigned char *>(p.o) +
+                                 ((int64_t)b * p.so_b + (int64_t)head * p.so_h + (p.q_start + row0_wave) * p.so_t) * ES;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4), c = lane & 15;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(epi + r * 256 + ((c ^ (r & 15)) * 16));
+      if (row0_wave + r < p.Tq)
+        *reinterpret_cast<u32x4 *>(const_cast<unsigned char *>(obase) + (int64_t)r * p.so_t * ES + c * 16) = v;
+    }
+    if (row_ok && p.lse && half == 0)
+      p.lse[(int64_t)b * p.sl_b + (int64_t)head * p.sl_h + p.q_start + row] =
+          l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+
   // o = a / l, lse = m + ln l; a row that saw nothing gets 0 and -inf.
   __device__ __forceinline__ void finish(const Params &p, int b, int head, int split) {
     const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -1225,6 +1259,8 @@ fa_fwd_kernel(Params p0) {
   constexpr int MBYTES = MODE == 1 ? MaskStager<NW>::MR * 256 : 16;  // staged mask blocks (MODE 1)
   __shared__ __attribute__((aligned(1024))) unsigned char m0[MBYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char m1[MBYTES];
+  // PERS: each wave's output rows on their way to HBM (Wave::finish_lds)
+  __shared__ __attribute__((aligned(1024))) unsigned char epi[PERS ? NW * 8192 : 16];
 
   // the wave index is uniform: keep it (and the LDS addresses derived from it) in SGPRs
   const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1326,7 +1362,7 @@ fa_fwd_kernel(Params p0) {
           if (t + 1 < wk.t_end) step(std::true_type{}, t + 1, k1, v1, m1, k0, v0, m0);
         }
       }
-      wv.finish(p, wk.b, head, wk.split);
+      wv.finish_lds(p, wk.b, head, wk.row0_blk + (wq / G) * kRowsWave, epi + wid * 8192);
       const int vb = item_of(k);
       if (vb < 0) break;
       wk = Work(p0, vb);
@@ -1356,6 +1392,15 @@ fa_fwd_kernel(Params p0) {
   // (not for the additive mask, whose kernel has no registers to spare for a second loop)
   if (MODE != 1 && cp.template src<true>(p, wk.t_end - 1).inside) run(std::integral_constant<bool, MODE != 1>{});
   else run(std::false_type{});
+  if constexpr (BF16 && D == 128 && DP == 1) {
+    // the tile buffers are free after the last step's barrier: 8 KiB of them per wave
+    if (p.n_splits == 0) {
+      const int bi = (wid >> 1) & 3;
+      unsigned char *buf = bi == 0 ? k0 : bi == 1 ? k1 : bi == 2 ? v0 : v1;
+      wv.finish_lds(p, wk.b, head, wk.row0_blk + (wq / G) * kRowsWave, buf + (wid & 1) * 8192);
+      return;
+    }
+  }
   wv.finish(p, wk.b, head, wk.split);
 }
 
