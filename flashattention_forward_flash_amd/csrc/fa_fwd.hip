@@ -1004,14 +1004,13 @@ struct Wave {
         const int c = 4 * db + g;
         *reinterpret_cast<u32x2 *>(epi + lq * 256 + ((c ^ (lq & 15)) * 16) + 8 * half) = pk;
       }
-    const unsigned char *obase = static_cast<unsigned char *>(p.o) +
-                                 ((int64_t)b * p.so_b + (int64_t)head * p.so_h + (p.q_start + row0_wave) * p.so_t) * ES;
+    unsigned char *obase = static_cast<unsigned char *>(p.o) +
+                           ((int64_t)b * p.so_b + (int64_t)head * p.so_h + (p.q_start + row0_wave) * p.so_t) * ES;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 8; ++i) {  // rows 4 i .. 4 i + 3, lane l: row 4 i + l / 16, chunk l % 16
       const int r = 4 * i + (lane >> 4), c = lane & 15;
       const u32x4 v = *reinterpret_cast<const u32x4 *>(epi + r * 256 + ((c ^ (r & 15)) * 16));
-      if (row0_wave + r < p.Tq)
-        *reinterpret_cast<u32x4 *>(const_cast<unsigned char *>(obase) + (int64_t)r * p.so_t * ES + c * 16) = v;
+      if (row0_wave + r < p.Tq) *reinterpret_cast<u32x4 *>(obase + (int64_t)r * p.so_t * ES + c * 16) = v;
     }
     if (row_ok && p.lse && half == 0)
       p.lse[(int64_t)b * p.sl_b + (int64_t)head * p.sl_h + p.q_start + row] =
