@@ -3,7 +3,7 @@
 "FlashAttention forward in C" section 2.4 and its tests chunk_invariant_with_q_offset and
 query_tile_and_batch_invariant: one call vs chunks with q_offset, every query-tile geometry,
 a sequence alone vs in a batch, and (here) the BHSD vs BSHD layouts.  Outputs are compared
-bit for bit after mapping -0.0 to +0.0.
+bit for bit (raw bits: the library writes every zero output as +0).
 """
 import numpy as np
 import pytest
@@ -123,3 +123,28 @@ def test_output_d_parts_equal_one_wave(d):
                                         causal=flags["causal"], window=flags.get("window", 0),
                                         sinks=z if flags.get("sinks") else None)
         compare(host(o), host(lse), o_ref, l_ref, "f32", f"d-parts {d} {Tq}x{Tk}")
+
+
+def test_long_causal_fp32_geometry_choice_keeps_bits():
+    """A 2,044-token causal fp32 call at 16/8 heads, d 128 (one layer of the 2,044-token
+    prefill): on a 256-CU device the automatic geometry takes the split-role kernel (32-row
+    one-head blocks, whose longest chain of tiles outweighs the total work of the 4-wave
+    geometry).  Its bits equal those of the 4-wave tiling (64 rows x 2 heads), of the one-wave
+    tiling, and of four chunked calls at the matching q_offset."""
+    B, Hq, Hkv, T, d = 1, 16, 8, 2044, 128
+    q, k, v, _ = make_inputs("inv-geom-2044/f32", B, Hq, Hkv, T, T, d, "f32")
+    tq, tk, tv = dev(q), dev(k), dev(v)
+    say("geometry choice 2044 f32")
+    o, lse = fa.forward(tq, tk, tv, causal=True)
+    for tiling in ((64, 2), (32, 1)):
+        o1, l1 = fa.forward(tq, tk, tv, causal=True, tiling=tiling)
+        torch.cuda.synchronize()
+        _same(o1, o, f"O tiling {tiling}")
+        _same(l1, lse, f"LSE tiling {tiling}")
+    start = 0
+    for n in (511, 511, 511, 511):
+        oc, lc = fa.forward(tq[:, :, start:start + n], tk, tv, q_offset=start, causal=True)
+        torch.cuda.synchronize()
+        _same(oc, o[:, :, start:start + n], f"O chunk {start}+{n}")
+        _same(lc, lse[:, :, start:start + n], f"LSE chunk {start}+{n}")
+        start += n
