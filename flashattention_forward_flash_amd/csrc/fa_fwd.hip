@@ -1761,8 +1761,9 @@ bool prefer_split_role(int64_t B, int64_t Hkv, int64_t group, int64_t Tq, int64_
     sum += t;
     longest = std::max(longest, t);
   }
-  const int64_t total = sum * B * Hkv * (group / heads);
-  return 4 * total < 3 * longest * (int64_t)ncu;
+  // (in double: the product can pass 2^63 for sizes the launch itself later refuses)
+  const double total = (double)sum * (double)B * (double)Hkv * (double)(group / heads);
+  return longest > 0 && 4.0 * total < 3.0 * (double)longest * ncu;
 }
 
 // Geometry of a split-KV call: the splits supply the parallelism, so a workgroup takes as many
