@@ -617,7 +617,7 @@ SQ_COUNTERS = (("SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU",
 
 
 def profile_commands(leg, steps=10, warmup=2):
-    """The rocprofv3 commands whose CSV output write_profile_summaries() reads (DIR = <repo>/gpurun_out/prof)."""
+    """The rocprofv3 commands whose CSV output write_profile_summaries() reads (DIR: any output directory)."""
     b = f"python3 <repo>/bench.py --leg {leg} --steps {steps} --warmup {warmup}"
     return [f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR/{leg}_trace -o run -- {b}",
             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/{leg}_FETCH_SIZE -o run -- {b}",
@@ -653,8 +653,8 @@ def _write_trace_summary(d, leg, src):
     flops = meta["flops"]
     lines = ["# fa_fwd kernel, bf16, d = 128, causal, B = 8, Hq = 32, Hkv = 8, Tq = Tk = 8192", "",
              "Kernel trace of the headline workload (one call = one step of `bench.py`).", "",
-             "Command (repository root on one MI355X, `cd /tmp && export TMPDIR=/tmp` first; DIR =",
-             "`<repo>/gpurun_out/prof`):", "", "```",
+             "Command (repository root on one MI355X, `cd /tmp && export TMPDIR=/tmp` first; DIR is",
+             "any output directory):", "", "```",
              f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR/{leg}_trace -o run -- python3 "
              f"<repo>/bench.py --leg {leg} --steps {meta['steps']} --warmup {meta['warmup']}",
              "python3 bench.py --profile-summary DIR   # writes this file", "```", "",
@@ -706,7 +706,7 @@ def write_profile_summaries(d):
              "Algorithmic bytes read Q, K, V (and the mask, sinks) once and write O (and LSE) once.",
              "",
              "Commands (repository root on one MI355X, `cd /tmp && export TMPDIR=/tmp` first; DIR is",
-             "`<repo>/gpurun_out/prof`; the calibration copy is `python3 <repo>/bench.py --copy-calibration`",
+             "any output directory; the calibration copy is `python3 <repo>/bench.py --copy-calibration`",
              "under the same two counter passes, into DIR/copy_FETCH_SIZE and DIR/copy_WRITE_SIZE); for",
              "each workload LEG below:",
              "",
